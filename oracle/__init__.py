@@ -1,0 +1,18 @@
+"""CPU oracle for paged extend attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The HIP library never reaches it, and it
+shares no code with the library.
+
+Parity status of each function (what pins it is listed in the tests):
+  extend_metadata   pinned: closed-form indptrs of the ragged batch
+  append_kv         pinned: gather after chunk-by-chunk append returns the
+                    contiguous sequence; untouched slots keep their canary bytes
+  gather_kv         pinned: same round trip, under shuffled page tables
+  extend_attention  pinned: zero-score closed forms (the PR's [1,2,3,4]),
+                    torch scaled_dot_product_attention on the full sequence
+                    (causal, GQA, band mask), W=1 and single-key identities,
+                    bitwise partition invariance
+"""
+from .paged_attention import (append_kv, extend_attention, extend_metadata, gather_kv,  # noqa: F401
+                               visible_range)
