@@ -1,0 +1,207 @@
+/*
+ * pkv.h -- C ABI of the paged extend-attention library (libpkv.so) for
+ * chunked prefill on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (AReno PR #642, "What does this PR do?"): a prompt that is
+ * prefilled in several chunks keeps its earlier chunks' K/V in a paged cache.
+ * Each query token of the current chunk attends, through the page table, to
+ * its request's cached prefix plus its own chunk, with the causal mask
+ * aligned bottom-right: token i of a chunk that follows P cached tokens sees
+ * key positions 0 .. P+i. New chunk K/V is appended into the pages first,
+ * continuing inside the last partly filled page.
+ *
+ * Argument vocabulary follows the pages' statement of the problem (AstrAI
+ * compare v1.3.12..925cbed: csrc/kernels/attn_types.cuh PagedAttentionParams,
+ * astrai/extension/attention_ops.py attn_paged_prefill, and
+ * astrai/inference/core/cache.py KVCache / PagePool.bind_tasks): paged K/V
+ * pools, a per-request page table (req_to_token), qo_indptr / kv_indptr
+ * prefix sums, prefix lengths, a window and the page size.
+ *
+ * Conventions shared by every entry point
+ *   - Status codes only; no exception crosses the ABI. On a non-zero status
+ *     pkv_last_error() returns a message for the calling thread. Every
+ *     argument is validated before anything is launched.
+ *   - The caller owns every buffer. The library never allocates device
+ *     memory and keeps no per-call state; all device work is asynchronous on
+ *     the given stream (a hipStream_t; NULL is the null stream).
+ *   - Element layouts (all contiguous, row-major):
+ *       q, out            [total_q, num_q_heads, head_dim]
+ *       k_new, v_new      [total_q, num_kv_heads, head_dim]
+ *       k_pool, v_pool    [num_pages, page_size, num_kv_heads, head_dim]
+ *       page_table        int32 [rows, page_table_stride]; entry [r][p] is the
+ *                         physical page holding logical page p (positions
+ *                         p*page_size .. p*page_size+page_size-1) of the
+ *                         request stored in row r. Row r of request b is
+ *                         req_pool_indices[b], or b when req_pool_indices is
+ *                         NULL. Only entries of positions < N_b are read.
+ *     Tokens of the batch are in request order: request b owns q/out/k_new/
+ *     v_new rows qo_indptr[b] .. qo_indptr[b+1]-1.
+ *   - Element type: bf16 (round-to-nearest-even outputs, fp32 accumulation)
+ *     or fp32, chosen by pkv_shape.dtype for all of q, pools, out.
+ *   - Page ids read from the page table outside [0, num_pages) are never
+ *     dereferenced: the attention reads such a key as zeros, the append drops
+ *     the write, and either sets the plan's device status word to
+ *     PKV_STATUS_BAD_PAGE (see pkv_read_status).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* pkv_stream_t; /* a hipStream_t */
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad length, inconsistent sizes   */
+  PKV_ERR_UNSUPPORTED = -2,      /* head_dim/dtype/group size not built, not gfx950 */
+  PKV_ERR_WORKSPACE = -3,        /* a caller buffer is smaller than required        */
+  PKV_ERR_HIP = -4               /* the HIP runtime reported an error               */
+};
+
+enum { PKV_DTYPE_BF16 = 0, PKV_DTYPE_FP32 = 1 };
+
+enum { PKV_STATUS_BAD_PAGE = 1 };
+
+/* Largest number of KV splits of one tile of query rows. */
+#define PKV_MAX_SPLITS 32
+
+/* Geometry of one attention layer's cache. */
+typedef struct pkv_shape {
+  int32_t num_q_heads;  /* Hq                                                   */
+  int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 128              */
+  int32_t head_dim;     /* D in {64, 128}                                       */
+  int32_t page_size;    /* ps >= 1 tokens per page                              */
+  int32_t num_pages;    /* pages in each pool                                   */
+  int32_t dtype;        /* PKV_DTYPE_BF16 or PKV_DTYPE_FP32                     */
+} pkv_shape;
+
+/* Result of build_extend_metadata: host scalars plus device pointers into the
+ * caller's meta_dev buffer. Plain data: copy it freely; it stays valid while
+ * meta_dev does. Reuse it for every layer of the step. */
+typedef struct pkv_plan {
+  int32_t batch;          /* B                                                  */
+  int32_t total_q;        /* sum of chunk lengths (rows of q / out)             */
+  int32_t max_q_len;      /* longest chunk                                      */
+  int32_t max_kv_len;     /* longest prefix + chunk                             */
+  int32_t n_items;        /* attention work items (one workgroup each)          */
+  int32_t n_split_rows;   /* query tokens computed as KV splits + combine       */
+  int32_t max_splits;     /* split stride of the partial buffers                */
+  int32_t window;         /* sliding window W (<= 0: none)                      */
+  pkv_shape shape;        /* the shape the plan was built for                   */
+  size_t workspace_bytes; /* scratch paged_extend_attn needs (0 if no splits)   */
+  /* device pointers (NULL after a host-only build) */
+  const int32_t* qo_indptr;   /* [B+1] exclusive prefix sum of chunk lengths    */
+  const int32_t* kv_indptr;   /* [B+1] exclusive prefix sum of prefix + chunk   */
+  const int32_t* prefix_lens; /* [B]                                            */
+  const void* items;          /* work list (library-private format)             */
+  const int32_t* split_rows;  /* [n_split_rows][2] token index, split count     */
+  int32_t* status;            /* one int32, zeroed by the metadata copy         */
+} pkv_plan;
+
+/*
+ * Size query for build_extend_metadata's buffers (host only, no GPU use).
+ *   prefix_lens_h, chunk_lens_h  host int32 [batch]: P_b >= 0, L_b >= 0
+ *   window                       W (<= 0: none)
+ *   decode_splits                KV splits for one-token chunks; 0 = choose
+ *   meta_bytes      out: bytes of meta_host and of meta_dev (same layout)
+ *   workspace_bytes out: bytes paged_extend_attn needs as workspace
+ * Returns PKV_OK, PKV_ERR_INVALID_ARGUMENT or PKV_ERR_UNSUPPORTED.
+ */
+int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                             const pkv_shape* shape, int32_t window, int32_t decode_splits,
+                             size_t* meta_bytes, size_t* workspace_bytes);
+
+/*
+ * build_extend_metadata -- step a1: per-step metadata, built once on the host
+ * and reused by every layer (AReno PR #642: prefix and total-KV lengths are
+ * carried in scheduler metadata; AstrAI compare, cache.py: kv_indptr is the
+ * prefix sum of per-request sequence lengths, precomputed once per step).
+ *
+ * Computes qo_indptr (exclusive cumsum of L_b), kv_indptr (exclusive cumsum
+ * of N_b = P_b + L_b), a copy of prefix_lens and the attention work list into
+ * meta_host, then enqueues one host-to-device copy of meta_host into meta_dev
+ * on `stream`. No device synchronisation.
+ *   meta_host   caller buffer of >= meta_bytes; it must stay unchanged until
+ *               the copy has executed (pinned memory makes the copy async).
+ *   meta_dev    device buffer of >= meta_bytes, or NULL for a host-only plan
+ *               (then no HIP call is made and the plan's device pointers are
+ *               NULL: useful for inspecting the plan without a GPU).
+ *   plan_out    receives the plan.
+ * Errors: PKV_ERR_INVALID_ARGUMENT (null pointers, batch < 1, negative
+ * lengths, int32 overflow of the sums, Hq % Hkv != 0, page_size < 1,
+ * num_pages < 1, decode_splits outside 0..PKV_MAX_SPLITS),
+ * PKV_ERR_UNSUPPORTED (head_dim not 64/128, dtype unknown, G > 128, device
+ * not gfx950), PKV_ERR_WORKSPACE (a buffer too small), PKV_ERR_HIP.
+ */
+int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                          const pkv_shape* shape, int32_t window, int32_t decode_splits,
+                          void* meta_host, size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes,
+                          pkv_plan* plan_out, pkv_stream_t stream);
+
+/*
+ * pkv_append -- step a2: write the chunk's new K/V into the pools
+ * (AReno PR #642: continue prefill inside the last allocated KV page;
+ * AstrAI compare, cache.py: the write slots of a prefill step are the
+ * req_to_token entries of positions start_pos .. seq_len-1).
+ *
+ * For token i of request b (position p = P_b + i) copies k_new/v_new row
+ * qo_indptr[b]+i into slot (page_table[row_b][p / page_size], p % page_size)
+ * of k_pool/v_pool. Bit copy; no other pool byte is written.
+ *   page_table_stride   entries per page-table row; must cover max_kv_len
+ *   req_pool_indices    device int32 [batch] or NULL (row b = b)
+ * Errors: PKV_ERR_INVALID_ARGUMENT (null pointer, plan/shape mismatch, stride
+ * too small), PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ */
+int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* page_table,
+               int32_t page_table_stride, const int32_t* req_pool_indices, const pkv_plan* plan,
+               const pkv_shape* shape, pkv_stream_t stream);
+
+/*
+ * paged_extend_attn -- steps a3..a9: attention of every chunk row over its
+ * request's prefix plus chunk (AReno PR #642; AstrAI compare,
+ * attn_paged_test.cu CPU reference for paged prefill: query head h reads KV
+ * head h / (Hq/Hkv); a request's causal offset is its total length minus its
+ * chunk length).
+ *
+ * Row i of request b, query head h, sees key positions j with
+ *   j <= P_b + i   and   (window <= 0 or j >= P_b + i - window + 1)
+ * and gets softmax(sm_scale * q.k_j) weighted V of those keys (0 if none).
+ *   qo_indptr, kv_indptr, prefix_lens   device int32 arrays ([B+1],[B+1],[B]);
+ *        NULL takes the plan's copies. They must describe the same batch as
+ *        the plan (kv_indptr[b+1]-kv_indptr[b] == prefix_lens[b] + L_b).
+ *   window     must equal the plan's window.
+ *   sm_scale   softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   out        [total_q, Hq, D] written for every row.
+ *   workspace  device scratch of >= plan->workspace_bytes (may be NULL when
+ *              that is 0): per-split partial results, combined by a second
+ *              kernel launched here when the plan has split rows.
+ * The pools must already hold the chunk's K/V (call pkv_append first).
+ * Errors: PKV_ERR_INVALID_ARGUMENT, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
+ * PKV_ERR_HIP.
+ */
+int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                      int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                      const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                      const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
+                      size_t workspace_bytes, pkv_stream_t stream);
+
+/* Copies the plan's device status word to *status_out after synchronising the
+ * stream (a diagnostic; not needed on the hot path). */
+int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream);
+
+/* Message for the calling thread's last non-zero status ("" if none). */
+const char* pkv_last_error(void);
+
+/* 1 if `device` is a gfx950 GPU the library was built for, 0 if not,
+ * negative status if the device cannot be queried. */
+int pkv_device_supported(int device);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,231 @@
+// C ABI of libpkv: argument validation, device checks and launches.
+// Declarations and the contract of every function are in include/pkv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+namespace {
+thread_local char g_error[512] = "";
+
+// Per-device "is gfx950" cache; the property query costs far more than a launch.
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+int query_device(int dev) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+int device_supported(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return query_device(dev);
+  std::call_once(g_dev_once[dev], [dev] { g_dev_ok[dev] = query_device(dev); });
+  return g_dev_ok[dev];
+}
+
+int check_current_device() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(PKV_ERR_HIP, "no current HIP device: %s", hipGetErrorString(e));
+  const int ok = device_supported(dev);
+  if (ok < 0) return set_error(PKV_ERR_HIP, "cannot query HIP device %d", dev);
+  if (ok == 0) return set_error(PKV_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X); this library targets gfx950 only", dev);
+  return PKV_OK;
+}
+
+bool same_shape(const pkv_shape& a, const pkv_shape& b) {
+  return a.num_q_heads == b.num_q_heads && a.num_kv_heads == b.num_kv_heads && a.head_dim == b.head_dim &&
+         a.page_size == b.page_size && a.num_pages == b.num_pages && a.dtype == b.dtype;
+}
+
+int check_plan(const pkv_plan* plan, const pkv_shape* shape, const char* who) {
+  if (!plan) return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: plan is NULL", who);
+  if (int st = validate_shape(shape)) return st;
+  if (!same_shape(plan->shape, *shape))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: shape differs from the one the plan was built for", who);
+  if (!plan->qo_indptr || !plan->kv_indptr || !plan->prefix_lens || !plan->items || !plan->status)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: plan has no device metadata (host-only build?)", who);
+  return PKV_OK;
+}
+
+int check_page_table(const int32_t* page_table, int32_t stride, const pkv_plan* plan, const char* who) {
+  if (!page_table) return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: page_table is NULL", who);
+  const int64_t need = (int64_t(plan->max_kv_len) + plan->shape.page_size - 1) / plan->shape.page_size;
+  if (stride < 1 || stride < need)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: page_table_stride %d cannot hold %lld pages (max_kv_len %d)",
+                     who, stride, (long long)need, plan->max_kv_len);
+  return PKV_OK;
+}
+}  // namespace
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error; }
+
+int pkv_device_supported(int device) {
+  const int ok = device_supported(device);
+  if (ok < 0) return set_error(PKV_ERR_HIP, "cannot query HIP device %d", device);
+  return ok;
+}
+
+int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                             const pkv_shape* shape, int32_t window, int32_t decode_splits, size_t* meta_bytes,
+                             size_t* workspace_bytes_out) {
+  g_error[0] = 0;
+  if (!meta_bytes || !workspace_bytes_out)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_extend_metadata_size: output pointers must not be NULL");
+  pkv_plan plan;
+  const int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, decode_splits, 0, nullptr, 0,
+                             &plan, meta_bytes);
+  if (st) return st;
+  *workspace_bytes_out = plan.workspace_bytes;
+  return PKV_OK;
+}
+
+int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                          const pkv_shape* shape, int32_t window, int32_t decode_splits, void* meta_host,
+                          size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes, pkv_plan* plan_out,
+                          pkv_stream_t stream) {
+  g_error[0] = 0;
+  if (!meta_host || !plan_out)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "build_extend_metadata: meta_host and plan_out must not be NULL");
+  size_t total = 0;
+  pkv_plan plan;
+  int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, decode_splits, 0, meta_host,
+                       meta_host_bytes, &plan, &total);
+  if (st) return st;
+  if (meta_dev) {
+    if (meta_dev_bytes < total)
+      return set_error(PKV_ERR_WORKSPACE, "meta_dev holds %zu bytes, %zu needed", meta_dev_bytes, total);
+    if ((st = check_current_device())) return st;
+    const hipError_t e =
+        hipMemcpyAsync(meta_dev, meta_host, total, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return set_error(PKV_ERR_HIP, "metadata copy failed: %s", hipGetErrorString(e));
+    const MetaLayout lay = meta_layout(batch, plan.n_items, plan.n_split_rows);
+    char* d = static_cast<char*>(meta_dev);
+    plan.qo_indptr = reinterpret_cast<const int32_t*>(d + lay.qo_indptr);
+    plan.kv_indptr = reinterpret_cast<const int32_t*>(d + lay.kv_indptr);
+    plan.prefix_lens = reinterpret_cast<const int32_t*>(d + lay.prefix_lens);
+    plan.items = d + lay.items;
+    plan.split_rows = plan.n_split_rows ? reinterpret_cast<const int32_t*>(d + lay.split_rows) : nullptr;
+    plan.status = reinterpret_cast<int32_t*>(d + lay.status);
+  }
+  *plan_out = plan;
+  return PKV_OK;
+}
+
+int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* page_table,
+               int32_t page_table_stride, const int32_t* req_pool_indices, const pkv_plan* plan,
+               const pkv_shape* shape, pkv_stream_t stream) {
+  g_error[0] = 0;
+  int st = check_plan(plan, shape, "pkv_append");
+  if (st) return st;
+  if ((st = check_page_table(page_table, page_table_stride, plan, "pkv_append"))) return st;
+  if (plan->total_q > 0 && (!k_new || !v_new || !k_pool || !v_pool))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_append: K/V pointers must not be NULL");
+  if ((st = check_current_device())) return st;
+  AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.page_table_stride = page_table_stride;
+  a.req_pool_indices = req_pool_indices;
+  a.qo_indptr = plan->qo_indptr;
+  a.prefix_lens = plan->prefix_lens;
+  a.status = plan->status;
+  a.batch = plan->batch;
+  a.total_q = plan->total_q;
+  a.shape = *shape;
+  return launch_append(a, stream);
+}
+
+int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                      int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                      const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                      const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
+                      size_t workspace_bytes, pkv_stream_t stream) {
+  g_error[0] = 0;
+  int st = check_plan(plan, shape, "paged_extend_attn");
+  if (st) return st;
+  if ((st = check_page_table(page_table, page_table_stride, plan, "paged_extend_attn"))) return st;
+  if (window != plan->window)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn: window %d differs from the plan's %d", window,
+                     plan->window);
+  if (plan->total_q > 0 && (!q || !k_pool || !v_pool || !out))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn: q, pools and out must not be NULL");
+  if (!(std::isfinite(sm_scale)))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn: sm_scale is not finite");
+  if (plan->workspace_bytes > 0) {
+    if (!workspace)
+      return set_error(PKV_ERR_WORKSPACE, "paged_extend_attn: the plan needs %zu workspace bytes, got NULL",
+                       plan->workspace_bytes);
+    if (workspace_bytes < plan->workspace_bytes)
+      return set_error(PKV_ERR_WORKSPACE, "paged_extend_attn: workspace holds %zu bytes, %zu needed",
+                       workspace_bytes, plan->workspace_bytes);
+  }
+  if ((st = check_current_device())) return st;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(shape->head_dim));
+  AttnArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.page_table_stride = page_table_stride;
+  a.req_pool_indices = req_pool_indices;
+  a.qo_indptr = qo_indptr ? qo_indptr : plan->qo_indptr;
+  a.kv_indptr = kv_indptr ? kv_indptr : plan->kv_indptr;
+  a.prefix_lens = prefix_lens ? prefix_lens : plan->prefix_lens;
+  a.items = static_cast<const WorkItem*>(plan->items);
+  a.split_rows = plan->split_rows;
+  a.status = plan->status;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.o_part = plan->n_split_rows ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ml_part = plan->n_split_rows
+                  ? reinterpret_cast<float*>(ws + workspace_o_bytes(plan->n_split_rows, shape->num_q_heads,
+                                                                    plan->max_splits, shape->head_dim))
+                  : nullptr;
+  a.n_items = plan->n_items;
+  a.n_split_rows = plan->n_split_rows;
+  a.max_splits = plan->max_splits;
+  a.total_q = plan->total_q;
+  a.window = window;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.shape = *shape;
+  return launch_extend_attn(a, stream);
+}
+
+int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream) {
+  g_error[0] = 0;
+  if (!plan || !plan->status || !status_out)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_read_status: plan with device metadata and status_out needed");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipMemcpy(status_out, plan->status, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return set_error(PKV_ERR_HIP, "pkv_read_status: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // extern "C"

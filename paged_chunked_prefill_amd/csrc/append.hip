@@ -1,0 +1,111 @@
+// KV append for chunked prefill: scatter each new token's K/V row into its
+// page slot.
+//
+// AReno PR #642 ("What does this PR do?"): a later prefill chunk continues
+// inside the last, partly filled KV page of its request. AstrAI compare
+// v1.3.12..925cbed (astrai/inference/core/cache.py, PagePool.bind_tasks):
+// the write slots of a prefill step are the page-table entries of positions
+// start_pos .. seq_len-1, and the backend writes k_buffer[out_cache_loc] = k.
+//
+// A token's K (or V) row of Hkv*D elements is contiguous both in k_new and in
+// its pool slot ([page][slot][Hkv][D]), so each thread moves one 16-byte
+// vector and a wave covers 1 KiB of consecutive source bytes: the copy is a
+// coalesced streaming scatter, bound by HBM bandwidth.
+#include <hip/hip_runtime.h>
+
+#include "pkv_internal.hpp"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct AppendParams {
+  const u32x4* k_new;
+  const u32x4* v_new;
+  u32x4* k_pool;
+  u32x4* v_pool;
+  const int32_t* page_table;
+  const int32_t* req_pool_indices;
+  const int32_t* qo_indptr;
+  const int32_t* prefix_lens;
+  int32_t* status;
+  int64_t total_vecs;      // total_q * vecs_per_token
+  int32_t vecs_per_token;  // Hkv * D * elem_bytes / 16
+  int32_t batch;
+  int32_t total_q;
+  int32_t page_size;
+  int32_t page_table_stride;
+  int32_t num_pages;
+};
+
+// Request owning global token t: the last b with qo_indptr[b] <= t (requests
+// with an empty chunk share their qo_indptr value with the next request).
+__device__ inline int find_request(const int32_t* qo_indptr, int batch, int t) {
+  int lo = 0, hi = batch;  // invariant: qo_indptr[lo] <= t < qo_indptr[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qo_indptr[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < p.total_vecs; i += stride) {
+    const int t = int(i / p.vecs_per_token);
+    const int v = int(i - int64_t(t) * p.vecs_per_token);
+    if (t >= p.total_q) break;
+    const int b = find_request(p.qo_indptr, p.batch, t);
+    const int pos = p.prefix_lens[b] + (t - p.qo_indptr[b]);
+    const int col = pos / p.page_size;
+    if (pos < 0 || col >= p.page_table_stride) {
+      atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+      continue;
+    }
+    const int row = p.req_pool_indices ? p.req_pool_indices[b] : b;
+    const int page = p.page_table[int64_t(row) * p.page_table_stride + col];
+    if (page < 0 || page >= p.num_pages) {
+      atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+      continue;
+    }
+    const int64_t slot = int64_t(page) * p.page_size + (pos - col * p.page_size);
+    const int64_t dst = slot * p.vecs_per_token + v;
+    p.k_pool[dst] = p.k_new[i];
+    p.v_pool[dst] = p.v_new[i];
+  }
+}
+
+}  // namespace
+
+int launch_append(const AppendArgs& a, void* stream) {
+  const int esize = a.shape.dtype == PKV_DTYPE_BF16 ? 2 : 4;
+  const int64_t row_bytes = int64_t(a.shape.num_kv_heads) * a.shape.head_dim * esize;
+  if (row_bytes % 16) return set_error(PKV_ERR_UNSUPPORTED, "K/V token rows must be a multiple of 16 bytes");
+  if (a.total_q == 0) return PKV_OK;
+  AppendParams p;
+  p.k_new = static_cast<const u32x4*>(a.k_new);
+  p.v_new = static_cast<const u32x4*>(a.v_new);
+  p.k_pool = static_cast<u32x4*>(a.k_pool);
+  p.v_pool = static_cast<u32x4*>(a.v_pool);
+  p.page_table = a.page_table;
+  p.req_pool_indices = a.req_pool_indices;
+  p.qo_indptr = a.qo_indptr;
+  p.prefix_lens = a.prefix_lens;
+  p.status = a.status;
+  p.vecs_per_token = int32_t(row_bytes / 16);
+  p.total_vecs = int64_t(a.total_q) * p.vecs_per_token;
+  p.batch = a.batch;
+  p.total_q = a.total_q;
+  p.page_size = a.shape.page_size;
+  p.page_table_stride = a.page_table_stride;
+  p.num_pages = a.shape.num_pages;
+  const int64_t want = (p.total_vecs + 255) / 256;
+  const int blocks = int(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(PKV_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv

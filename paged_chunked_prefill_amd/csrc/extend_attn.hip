@@ -1,0 +1,634 @@
+// Paged extend attention for chunked prefill on CDNA4 (gfx950).
+//
+// What is computed (AReno PR #642, "What does this PR do?"): every query row of
+// the current chunk attends to its request's cached prefix plus its own chunk,
+// with the causal mask aligned bottom-right -- row i of a chunk that follows P
+// cached tokens sees key positions 0..P+i -- optionally limited to a sliding
+// window of W positions ending at its own. Query head h reads KV head
+// h / (Hq/Hkv) (AstrAI compare v1.3.12..925cbed, attn_paged_test.cu CPU
+// reference for paged prefill).
+//
+// How (one workgroup per planner work item = GQA-packed query tile x key range):
+//  * The tile's rows are (token, query head) pairs of one KV head; four waves
+//    own 32 rows each, so the K/V tile staged in LDS serves all G heads.
+//  * Keys are walked in tiles aligned to absolute positions. Each key's page
+//    is looked up in the page table; its D-row is read from the pool with
+//    16-byte loads into registers (prefetching the next tile while the
+//    current one is computed) and then written to the other LDS stage.
+//    Positions outside the item's key range are zero-filled, never loaded.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K rows come from LDS, the wave's
+//    Q rows stay in registers. Each lane then holds 16 scores of one query row
+//    per 32-key block, so the row max needs one cross-half permlane swap and
+//    the exponentials are plain per-lane VALU work (exp2 with the softmax
+//    scale folded with log2 e).
+//  * O^T += V^T P^T on the same MFMA: P^T is the score accumulator converted
+//    to bf16 in place (its register layout is already the B-operand layout);
+//    V^T fragments come from LDS through ds_read_b64_tr_b16, which transposes
+//    4x16-element blocks on the fly, so V needs no transposed copy.
+//  * Online softmax (running max and sum per row); split items store the
+//    unnormalised output with (max, sum) and a combine kernel merges splits.
+// The fp32 instantiation uses v_mfma_f32_32x32x2f32 with the same data flow.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv_internal.hpp"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Params {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* req_pool_indices;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* prefix_lens;
+  const WorkItem* items;
+  int32_t* status;
+  void* out;
+  float* o_part;
+  float* ml_part;
+  int32_t page_table_stride;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t window;
+  int32_t total_q;
+  int32_t max_splits;
+  float scale_log2;
+};
+
+// Value of the same query row held by the other half of the wave (lanes l and
+// l^32 hold the two halves of one row's scores).
+__device__ inline float other_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float other_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-item geometry shared by both instantiations.
+struct ItemView {
+  int req, kv_head, q_begin, q_count, kv_begin, kv_end, split, part_row;
+  int prefix, qo, pt_row;
+};
+
+__device__ inline ItemView load_item(const Params& p) {
+  const WorkItem it = p.items[blockIdx.x];
+  ItemView v;
+  v.req = it.req;
+  v.kv_head = it.kv_head;
+  v.q_begin = it.q_begin;
+  v.split = it.split;
+  v.part_row = it.part_row;
+  v.prefix = p.prefix_lens[it.req];
+  v.qo = p.qo_indptr[it.req];
+  const int chunk = p.qo_indptr[it.req + 1] - v.qo;
+  const int kv_len = p.kv_indptr[it.req + 1] - p.kv_indptr[it.req];
+  // never step outside the request, whatever the work item says
+  v.q_count = min(it.q_count, chunk - it.q_begin);
+  v.kv_begin = max(it.kv_begin, 0);
+  const int64_t addressable = int64_t(p.page_table_stride) * p.page_size;
+  v.kv_end = int(min(int64_t(min(it.kv_end, kv_len)), addressable));
+  v.pt_row = p.req_pool_indices ? p.req_pool_indices[it.req] : it.req;
+  return v;
+}
+
+// Is key position j visible from the query at absolute position qpos?
+__device__ inline bool key_visible(int j, int qpos, int kv_begin, int kv_end, int window) {
+  return j >= kv_begin && j < kv_end && j <= qpos && (window <= 0 || j > qpos - window);
+}
+
+// ---------------------------------------------------------------------------
+// bf16: 64-key tiles, 32x32x16 MFMA
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct Bf16Tile {
+  static constexpr int BC = kTileKeysBf16;         // keys per tile
+  static constexpr int KPITCH = D * 2 + 16;        // LDS bytes per K row (16 B pad: b128 reads conflict-free)
+  static constexpr int VPITCH = D * 2 + 32;        // LDS bytes per V row (32 B pad: transposing reads)
+  static constexpr int KBYTES = BC * KPITCH;
+  static constexpr int STAGE = KBYTES + BC * VPITCH;
+  static constexpr int CHUNKS = D / 8;             // 16-byte chunks per key row
+  static constexpr int KEYS_PER_PASS = 256 / CHUNKS;
+  static constexpr int LOADS = BC / KEYS_PER_PASS; // 16-byte loads per thread per tensor
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
+  using T = Bf16Tile<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+
+  const ItemView it = load_item(p);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int G = p.group;
+
+  // this lane's query row: tile row r = token * G + head-in-group
+  const int r = wave * 32 + l32;
+  const int tok = r / G, gh = r - tok * G;
+  const int gtok = it.qo + it.q_begin + tok;                 // global token index
+  const bool row_live = tok < it.q_count && gtok < p.total_q;
+  const int qpos = it.prefix + it.q_begin + tok;             // absolute query position
+  const int head = it.kv_head * G + gh;
+  const bool wave_live = wave * 32 < it.q_count * G;
+  const int qpos_first = it.prefix + it.q_begin;
+  const int qpos_last = it.prefix + it.q_begin + it.q_count - 1;
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7]
+  bf16x8 qf[T::KSTEPS];
+  {
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
+                                                       (int64_t(gtok) * p.num_q_heads + head) * D + 8 * half);
+#pragma unroll
+    for (int ks = 0; ks < T::KSTEPS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_live) v = qrow[2 * ks];
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 o[T::DBLK];
+#pragma unroll
+  for (int db = 0; db < T::DBLK; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;  // running max of this row's raw scores
+  float l_run = 0.f;        // running sum of exp over the keys this lane holds
+
+  const int t0 = (it.kv_begin / T::BC) * T::BC;
+  const int ntiles = it.kv_end > it.kv_begin ? (it.kv_end - t0 + T::BC - 1) / T::BC : 0;
+  const int32_t* pt = p.page_table + int64_t(it.pt_row) * p.page_table_stride;
+  const uint16_t* kpool = static_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(p.v_pool);
+  const int chunk = tid % T::CHUNKS, key_in_pass = tid / T::CHUNKS;
+  const int64_t row_elems = int64_t(p.num_kv_heads) * D;
+
+  u32x4 kreg[T::LOADS], vreg[T::LOADS];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int j = kv0 + key_in_pass + i * T::KEYS_PER_PASS;
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (j >= it.kv_begin && j < it.kv_end) {
+        const int col = j / p.page_size;
+        const int page = pt[col];
+        if (page >= 0 && page < p.num_pages) {
+          const int64_t off = (int64_t(page) * p.page_size + (j - col * p.page_size)) * row_elems +
+                              int64_t(it.kv_head) * D + 8 * chunk;
+          kreg[i] = *reinterpret_cast<const u32x4*>(kpool + off);
+          vreg[i] = *reinterpret_cast<const u32x4*>(vpool + off);
+        } else {
+          atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* kb = smem + stage * T::STAGE;
+    char* vb = kb + T::KBYTES;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int kr = key_in_pass + i * T::KEYS_PER_PASS;
+      *reinterpret_cast<u32x4*>(kb + kr * T::KPITCH + chunk * 16) = kreg[i];
+      *reinterpret_cast<u32x4*>(vb + kr * T::VPITCH + chunk * 16) = vreg[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(t0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  // lane roles in the transposing V reads: group g4 of 16 lanes, element e, column quad q4
+  const int g4 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+  const float c = p.scale_log2;
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int kv0 = t0 + tile * T::BC;
+    const int stage = tile & 1;
+    if (tile + 1 < ntiles) load_tile(kv0 + T::BC);
+
+    if (wave_live) {
+      const char* kb = smem + stage * T::STAGE;
+      const char* vb = kb + T::KBYTES;
+
+      // S^T[key][row] for two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        s[kb2] = f32x16{};
+        const char* krow = kb + (32 * kb2 + l32) * T::KPITCH + 16 * half;
+#pragma unroll
+        for (int ks = 0; ks < T::KSTEPS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
+        }
+      }
+
+      // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
+      const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
+                        (p.window <= 0 || kv0 > qpos_last - p.window);
+      if (!full) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = kv0 + 32 * kb2 + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (!key_visible(key, qpos, it.kv_begin, it.kv_end, p.window)) s[kb2][j] = -INFINITY;
+          }
+      }
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
+      mx = other_half_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_off = m_new == -INFINITY ? 0.f : m_new * c;
+      const float alpha = fast_exp2(m_run * c - m_off);
+
+      // P = exp2(S*c - m) in bf16, laid out as the B operand of O^T += V^T P^T
+      bf16x8 pb[2][2];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float pj = fast_exp2(fmaf(s[kb2][j], c, -m_off));
+          lsum += pj;
+          pb[kb2][j >> 3][j & 7] = (__bf16)pj;
+        }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
+
+#pragma unroll
+      for (int db = 0; db < T::DBLK; ++db) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2) {
+            // lane 16g+4e+q reads 4 d-values of key row (32kb2+16m2+4(g/2)+e [+8]) at d = 32db+16(g%2)+4q;
+            // the transpose hands lane l the keys 32kb2+16m2+8r+4(l/32)+e at d = 32db + l%32
+            const int krow = 32 * kb2 + 16 * m2 + 4 * (g4 >> 1) + e4;
+            const char* vaddr = vb + krow * T::VPITCH + (32 * db + 16 * (g4 & 1) + 4 * q4) * 2;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vaddr));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vaddr + 8 * T::VPITCH));
+            const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a32), pb[kb2][m2], o[db], 0,
+                                                            0, 0);
+          }
+        }
+      }
+    }
+
+    if (tile + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  const float l_tot = other_half_sum(l_run);
+  if (!row_live) return;
+  // O^T accumulator: register j of block db is d = 32db + 8(j/4) + 4half + j%4 of this lane's row
+  if (it.part_row < 0) {
+    // divide (not multiply by a reciprocal): exact whenever the quotient is representable
+    const float den = l_tot > 0.f ? l_tot : INFINITY;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + (int64_t(gtok) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 v;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = (__bf16)(o[db][4 * jj + x] / den);
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jj + 4 * half) = __builtin_bit_cast(u32x2, v);
+      }
+  } else {
+    const int64_t slot = int64_t(it.part_row + tok) * p.num_q_heads + head;
+    const int64_t prow = slot * p.max_splits + it.split;
+    float* op = p.o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * jj + 4 * half) = v;
+      }
+    if (half == 0) {
+      p.ml_part[prow * 2] = m_run == -INFINITY ? -INFINITY : m_run * c;
+      p.ml_part[prow * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32: 32-key tiles, 32x32x2 fp32 MFMA (same data flow, scalar operands)
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct F32Tile {
+  static constexpr int BC = kTileKeysF32;
+  static constexpr int KPITCH = D + 1;             // floats per K row (odd pitch: column reads conflict-free)
+  static constexpr int VPITCH = D;                 // floats per V row (row reads)
+  static constexpr int KFLOATS = BC * KPITCH;
+  static constexpr int STAGE = KFLOATS + BC * VPITCH;  // floats
+  static constexpr int CHUNKS = D / 4;             // 16-byte chunks per key row
+  static constexpr int KEYS_PER_PASS = 256 / CHUNKS;
+  static constexpr int LOADS = BC / KEYS_PER_PASS;
+  static constexpr int KSTEPS = D / 2;
+  static constexpr int DBLK = D / 32;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
+  using T = F32Tile<D>;
+  __shared__ float smem[2 * T::STAGE];
+
+  const ItemView it = load_item(p);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int G = p.group;
+  const int r = wave * 32 + l32;
+  const int tok = r / G, gh = r - tok * G;
+  const int gtok = it.qo + it.q_begin + tok;
+  const bool row_live = tok < it.q_count && gtok < p.total_q;
+  const int qpos = it.prefix + it.q_begin + tok;
+  const int head = it.kv_head * G + gh;
+  const bool wave_live = wave * 32 < it.q_count * G;
+
+  // Q operand: lane holds q[row][2ks + half]
+  float qf[T::KSTEPS];
+  {
+    const float* qrow = static_cast<const float*>(p.q) + (int64_t(gtok) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < T::KSTEPS; ++ks) qf[ks] = row_live ? qrow[2 * ks + half] : 0.f;
+  }
+
+  f32x16 o[T::DBLK];
+#pragma unroll
+  for (int db = 0; db < T::DBLK; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int t0 = (it.kv_begin / T::BC) * T::BC;
+  const int ntiles = it.kv_end > it.kv_begin ? (it.kv_end - t0 + T::BC - 1) / T::BC : 0;
+  const int32_t* pt = p.page_table + int64_t(it.pt_row) * p.page_table_stride;
+  const float* kpool = static_cast<const float*>(p.k_pool);
+  const float* vpool = static_cast<const float*>(p.v_pool);
+  const int chunk = tid % T::CHUNKS, key_in_pass = tid / T::CHUNKS;
+  const int64_t row_elems = int64_t(p.num_kv_heads) * D;
+
+  f32x4 kreg[T::LOADS], vreg[T::LOADS];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int j = kv0 + key_in_pass + i * T::KEYS_PER_PASS;
+      kreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j >= it.kv_begin && j < it.kv_end) {
+        const int col = j / p.page_size;
+        const int page = pt[col];
+        if (page >= 0 && page < p.num_pages) {
+          const int64_t off = (int64_t(page) * p.page_size + (j - col * p.page_size)) * row_elems +
+                              int64_t(it.kv_head) * D + 4 * chunk;
+          kreg[i] = *reinterpret_cast<const f32x4*>(kpool + off);
+          vreg[i] = *reinterpret_cast<const f32x4*>(vpool + off);
+        } else {
+          atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    float* kb = smem + stage * T::STAGE;
+    float* vb = kb + T::KFLOATS;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int kr = key_in_pass + i * T::KEYS_PER_PASS;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) kb[kr * T::KPITCH + 4 * chunk + x] = kreg[i][x];
+      *reinterpret_cast<f32x4*>(vb + kr * T::VPITCH + 4 * chunk) = vreg[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(t0);
+    store_tile(0);
+  }
+  __syncthreads();
+  const float c = p.scale_log2;
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int kv0 = t0 + tile * T::BC;
+    const int stage = tile & 1;
+    if (tile + 1 < ntiles) load_tile(kv0 + T::BC);
+    if (wave_live) {
+      const float* kb = smem + stage * T::STAGE;
+      const float* vb = kb + T::KFLOATS;
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < T::KSTEPS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kb[l32 * T::KPITCH + 2 * ks + half], qf[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = kv0 + 8 * (j >> 2) + 4 * half + (j & 3);
+        if (!key_visible(key, qpos, it.kv_begin, it.kv_end, p.window)) s[j] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[j]);
+      mx = other_half_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_off = m_new == -INFINITY ? 0.f : m_new * c;
+      const float alpha = fast_exp2(m_run * c - m_off);
+      float lsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        s[j] = fast_exp2(fmaf(s[j], c, -m_off));
+        lsum += s[j];
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < T::DBLK; ++db) {
+        o[db] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = 8 * (j >> 2) + 4 * half + (j & 3);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vb[key * T::VPITCH + 32 * db + l32], s[j], o[db], 0, 0, 0);
+        }
+      }
+    }
+    if (tile + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  const float l_tot = other_half_sum(l_run);
+  if (!row_live) return;
+  if (it.part_row < 0) {
+    const float den = l_tot > 0.f ? l_tot : INFINITY;
+    float* orow = static_cast<float*>(p.out) + (int64_t(gtok) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {o[db][4 * jj] / den, o[db][4 * jj + 1] / den, o[db][4 * jj + 2] / den,
+                         o[db][4 * jj + 3] / den};
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * jj + 4 * half) = v;
+      }
+  } else {
+    const int64_t slot = int64_t(it.part_row + tok) * p.num_q_heads + head;
+    const int64_t prow = slot * p.max_splits + it.split;
+    float* op = p.o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * jj + 4 * half) = v;
+      }
+    if (half == 0) {
+      p.ml_part[prow * 2] = m_run == -INFINITY ? -INFINITY : m_run * c;
+      p.ml_part[prow * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split combine: O = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k
+// ---------------------------------------------------------------------------
+
+struct CombineParams {
+  const float* o_part;
+  const float* ml_part;
+  const int32_t* split_rows;
+  void* out;
+  int32_t num_q_heads;
+  int32_t max_splits;
+  int32_t total_q;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
+  const int slot = blockIdx.x;
+  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (head >= p.num_q_heads) return;
+  const int token = p.split_rows[2 * slot];
+  const int ns = min(p.split_rows[2 * slot + 1], p.max_splits);
+  if (token < 0 || token >= p.total_q) return;
+  const int64_t base = (int64_t(slot) * p.num_q_heads + head) * p.max_splits;
+  float M = -INFINITY;
+  for (int k = 0; k < ns; ++k) M = fmaxf(M, p.ml_part[(base + k) * 2]);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int x = 0; x < PER; ++x) acc[x] = 0.f;
+  float den = 0.f;
+  for (int k = 0; k < ns; ++k) {
+    const float mk = p.ml_part[(base + k) * 2];
+    const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
+    den += w * p.ml_part[(base + k) * 2 + 1];
+    const float* op = p.o_part + (base + k) * D;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) acc[x] = fmaf(w, op[lane + 64 * x], acc[x]);
+  }
+  if (!(den > 0.f)) den = INFINITY;  // no visible key: output 0
+  const int64_t orow = (int64_t(token) * p.num_q_heads + head) * D;
+#pragma unroll
+  for (int x = 0; x < PER; ++x) {
+    if (BF16)
+      static_cast<__bf16*>(p.out)[orow + lane + 64 * x] = (__bf16)(acc[x] / den);
+    else
+      static_cast<float*>(p.out)[orow + lane + 64 * x] = acc[x] / den;
+  }
+}
+
+template <int D, bool BF16>
+void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
+  if (a.n_items > 0) {
+    if (BF16)
+      hipLaunchKernelGGL(extend_attn_bf16<D>, dim3(a.n_items), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL(extend_attn_f32<D>, dim3(a.n_items), dim3(256), 0, st, p);
+  }
+  if (a.n_split_rows > 0) {
+    CombineParams cp;
+    cp.o_part = a.o_part;
+    cp.ml_part = a.ml_part;
+    cp.split_rows = a.split_rows;
+    cp.out = a.out;
+    cp.num_q_heads = a.shape.num_q_heads;
+    cp.max_splits = a.max_splits;
+    cp.total_q = a.total_q;
+    hipLaunchKernelGGL((combine_splits<D, BF16>), dim3(a.n_split_rows, (a.shape.num_q_heads + 3) / 4), dim3(256),
+                       0, st, cp);
+  }
+}
+
+}  // namespace
+
+int launch_extend_attn(const AttnArgs& a, void* stream) {
+  Params p;
+  p.q = a.q;
+  p.k_pool = a.k_pool;
+  p.v_pool = a.v_pool;
+  p.page_table = a.page_table;
+  p.req_pool_indices = a.req_pool_indices;
+  p.qo_indptr = a.qo_indptr;
+  p.kv_indptr = a.kv_indptr;
+  p.prefix_lens = a.prefix_lens;
+  p.items = a.items;
+  p.status = a.status;
+  p.out = a.out;
+  p.o_part = a.o_part;
+  p.ml_part = a.ml_part;
+  p.page_table_stride = a.page_table_stride;
+  p.num_q_heads = a.shape.num_q_heads;
+  p.num_kv_heads = a.shape.num_kv_heads;
+  p.group = a.shape.num_q_heads / a.shape.num_kv_heads;
+  p.page_size = a.shape.page_size;
+  p.num_pages = a.shape.num_pages;
+  p.window = a.window;
+  p.total_q = a.total_q;
+  p.max_splits = a.max_splits;
+  p.scale_log2 = a.scale_log2;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = a.shape.dtype == PKV_DTYPE_BF16;
+  if (a.shape.head_dim == 128) {
+    if (bf16) launch_typed<128, true>(p, a, st); else launch_typed<128, false>(p, a, st);
+  } else {
+    if (bf16) launch_typed<64, true>(p, a, st); else launch_typed<64, false>(p, a, st);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv

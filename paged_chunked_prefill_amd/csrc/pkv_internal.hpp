@@ -1,0 +1,130 @@
+// Internal definitions shared by the host planner and the HIP kernels of
+// libpkv. Not part of the public ABI (include/pkv.h is).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Query-head rows per attention workgroup: four waves of 32 rows each. Rows
+// are (token, head-in-group) pairs of one KV head, token-major, so a tile
+// holds ROWS / G consecutive chunk tokens.
+constexpr int kWaves = 4;
+constexpr int kRows = 32 * kWaves;
+// Keys per KV tile staged in LDS (bf16 / fp32 instantiations).
+constexpr int kTileKeysBf16 = 64;
+constexpr int kTileKeysF32 = 32;
+// Every split of a one-token row covers whole 64-key blocks, so the tile
+// boundaries of both instantiations stay aligned to absolute positions.
+constexpr int kSplitGranule = 64;
+
+// One unit of attention work = one workgroup: a tile of consecutive chunk
+// tokens of one request, all G query heads of one KV head, over the key
+// positions [kv_begin, kv_end) (the whole visible range, or one split of it).
+struct alignas(16) WorkItem {
+  int32_t req;       // request index b
+  int32_t kv_head;   // KV head hk; query heads hk*G .. hk*G+G-1
+  int32_t q_begin;   // first chunk token of the tile (0-based within the chunk)
+  int32_t q_count;   // tokens in the tile (>= 1)
+  int32_t kv_begin;  // first key position this item covers
+  int32_t kv_end;    // one past the last key position (<= N_b)
+  int32_t split;     // split index within the tile's row (0 when unsplit)
+  int32_t part_row;  // -1: write `out`; else partial slot of the tile's first token
+};
+static_assert(sizeof(WorkItem) == 32, "work item layout");
+
+// Byte offsets of the sections of the metadata buffer (host staging and its
+// device copy share the layout). Each section starts on a 256-byte boundary.
+struct MetaLayout {
+  size_t qo_indptr, kv_indptr, prefix_lens, items, split_rows, status, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline MetaLayout meta_layout(int32_t batch, int32_t n_items, int32_t n_split_rows) {
+  MetaLayout m;
+  size_t off = 0;
+  m.qo_indptr = off;   off = align256(off + sizeof(int32_t) * (size_t(batch) + 1));
+  m.kv_indptr = off;   off = align256(off + sizeof(int32_t) * (size_t(batch) + 1));
+  m.prefix_lens = off; off = align256(off + sizeof(int32_t) * size_t(batch));
+  m.items = off;       off = align256(off + sizeof(WorkItem) * size_t(n_items));
+  m.split_rows = off;  off = align256(off + 2 * sizeof(int32_t) * size_t(n_split_rows));
+  m.status = off;      off = align256(off + sizeof(int32_t));
+  m.total = off;
+  return m;
+}
+
+// Split partials in the workspace: for partial slot s, query head h, split k
+//   o_part [s][h][k][D] fp32 (unnormalised output)
+//   ml_part[s][h][k][2] fp32 (running max in log2 units, running sum)
+inline size_t workspace_o_bytes(int32_t n_split_rows, int32_t hq, int32_t max_splits, int32_t d) {
+  return align256(sizeof(float) * size_t(n_split_rows) * hq * max_splits * d);
+}
+inline size_t workspace_bytes(int32_t n_split_rows, int32_t hq, int32_t max_splits, int32_t d) {
+  if (n_split_rows == 0) return 0;
+  return workspace_o_bytes(n_split_rows, hq, max_splits, d) +
+         align256(sizeof(float) * size_t(n_split_rows) * hq * max_splits * 2);
+}
+
+// Host planner (planner.cpp). Fills `meta_host` (may be NULL for a size query)
+// and the host fields of `plan`. Returns a PKV status; sets the error text.
+int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_lens, const pkv_shape* shape,
+                int32_t window, int32_t decode_splits, int32_t num_cus, void* meta_host, size_t meta_host_bytes,
+                pkv_plan* plan, size_t* meta_bytes_out);
+
+int validate_shape(const pkv_shape* shape);
+
+// Thread-local error text (api.hip).
+int set_error(int status, const char* fmt, ...);
+
+// Kernel launchers (append.hip, extend_attn.hip). Arguments are validated by
+// the callers in api.hip.
+struct AttnArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  int32_t page_table_stride;
+  const int32_t* req_pool_indices;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* prefix_lens;
+  const WorkItem* items;
+  const int32_t* split_rows;
+  int32_t* status;
+  void* out;
+  float* o_part;
+  float* ml_part;
+  int32_t n_items;
+  int32_t n_split_rows;
+  int32_t max_splits;
+  int32_t total_q;
+  int32_t window;
+  float scale_log2;   // softmax scale * log2(e)
+  pkv_shape shape;
+};
+
+int launch_extend_attn(const AttnArgs& a, void* stream);
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* page_table;
+  int32_t page_table_stride;
+  const int32_t* req_pool_indices;
+  const int32_t* qo_indptr;
+  const int32_t* prefix_lens;
+  int32_t* status;
+  int32_t batch;
+  int32_t total_q;
+  pkv_shape shape;
+};
+
+int launch_append(const AppendArgs& a, void* stream);
+
+}  // namespace pkv

@@ -1,0 +1,212 @@
+// Host-side step metadata for paged extend attention: indptrs, prefix lengths
+// and the attention work list. Pure C++; no HIP call is made here.
+//
+// AReno PR #642 ("What does this PR do?") carries per-request prefix and
+// total-KV lengths in the step metadata so that one attention call serves a
+// batch of mixed prefix/chunk lengths. AstrAI compare v1.3.12..925cbed
+// (astrai/inference/core/cache.py, KVCache and PagePool.bind_tasks) builds
+// kv_indptr once per step as the prefix sum of per-request total lengths so
+// that no layer rebuilds it; csrc/kernels/attn_dispatchers.cuh
+// (compute_num_splits) sizes the KV splits of one-token rows from the
+// compute-unit count. This planner keeps those roles and adds what a
+// work-list launch needs: tiles of GQA-packed query rows, their visible key
+// ranges (causal and window bounds), and split slots for the combine step.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+int validate_shape(const pkv_shape* s) {
+  if (!s) return set_error(PKV_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hkv=%d)", s->num_q_heads,
+                     s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                     s->num_q_heads, s->num_kv_heads);
+  if (s->page_size < 1) return set_error(PKV_ERR_INVALID_ARGUMENT, "page_size must be >= 1 (got %d)", s->page_size);
+  if (s->num_pages < 1) return set_error(PKV_ERR_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", s->num_pages);
+  if (s->dtype != PKV_DTYPE_BF16 && s->dtype != PKV_DTYPE_FP32)
+    return set_error(PKV_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = fp32)", s->dtype);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return set_error(PKV_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", s->head_dim);
+  if (s->num_q_heads / s->num_kv_heads > kRows)
+    return set_error(PKV_ERR_UNSUPPORTED, "GQA group size %d exceeds %d", s->num_q_heads / s->num_kv_heads, kRows);
+  return PKV_OK;
+}
+
+namespace {
+
+struct Tile {
+  int32_t req, q_begin, q_count, kv_lo, kv_hi;
+  bool one_token;  // the request's whole chunk is a single token
+};
+
+int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
+
+}  // namespace
+
+int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_lens, const pkv_shape* shape,
+                int32_t window, int32_t decode_splits, int32_t num_cus, void* meta_host, size_t meta_host_bytes,
+                pkv_plan* plan, size_t* meta_bytes_out) {
+  if (int st = validate_shape(shape)) return st;
+  if (batch < 1) return set_error(PKV_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
+  if (!prefix_lens || !chunk_lens) return set_error(PKV_ERR_INVALID_ARGUMENT, "length arrays must not be NULL");
+  if (decode_splits < 0 || decode_splits > PKV_MAX_SPLITS)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "decode_splits must be in 0..%d (got %d)", PKV_MAX_SPLITS,
+                     decode_splits);
+  if (num_cus < 1) num_cus = 256;
+
+  const int32_t hq = shape->num_q_heads, hkv = shape->num_kv_heads;
+  const int32_t group = hq / hkv;
+  const int32_t tile_tokens = std::max(1, kRows / group);
+
+  // ---- per-request sums (int32 range checked in 64-bit)
+  int64_t total_q = 0, total_kv = 0;
+  int32_t max_q = 0, max_kv = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t P = prefix_lens[b], L = chunk_lens[b];
+    if (P < 0 || L < 0)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "request %d: negative length (prefix %lld, chunk %lld)", b,
+                       (long long)P, (long long)L);
+    const int64_t N = P + L;
+    if (N > INT32_MAX) return set_error(PKV_ERR_INVALID_ARGUMENT, "request %d: prefix + chunk overflows int32", b);
+    total_q += L;
+    total_kv += N;
+    if (total_q > INT32_MAX || total_kv > INT32_MAX)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "batch token counts overflow int32");
+    max_q = std::max<int32_t>(max_q, int32_t(L));
+    max_kv = std::max<int32_t>(max_kv, int32_t(N));
+  }
+
+  std::vector<int32_t> qo_start(batch, 0);
+  for (int32_t b = 1; b < batch; ++b) qo_start[b] = qo_start[b - 1] + chunk_lens[b - 1];
+
+  // ---- tiles of GQA-packed query rows and their visible key ranges
+  std::vector<Tile> tiles;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t P = prefix_lens[b], L = chunk_lens[b];
+    for (int32_t q0 = 0; q0 < L; q0 += tile_tokens) {
+      Tile t;
+      t.req = b;
+      t.q_begin = q0;
+      t.q_count = std::min(tile_tokens, L - q0);
+      // the tile's first row sees keys from max(0, P+q0-W+1); its last row up to P+q0+count-1
+      t.kv_lo = window > 0 ? int32_t(std::max<int64_t>(0, int64_t(P) + q0 - window + 1)) : 0;
+      t.kv_hi = P + q0 + t.q_count;
+      t.one_token = (L == 1);
+      tiles.push_back(t);
+    }
+  }
+
+  // ---- KV splits for one-token rows (explicit count, or sized to fill the GPU)
+  int32_t base_items = 0, n_one = 0;
+  for (const Tile& t : tiles) {
+    base_items += hkv;
+    n_one += t.one_token;
+  }
+  int32_t auto_splits = 1;
+  if (decode_splits == 0 && n_one > 0 && base_items > 0)
+    auto_splits = std::min<int32_t>(PKV_MAX_SPLITS, std::max<int32_t>(1, ceil_div(2LL * num_cus, base_items)));
+
+  std::vector<WorkItem> items;
+  std::vector<int32_t> split_rows;  // pairs (token, splits)
+  int32_t n_split_rows = 0, max_splits = 1;
+  for (const Tile& t : tiles) {
+    const int32_t g0 = t.kv_lo / kSplitGranule;
+    const int32_t g1 = ceil_div(t.kv_hi, kSplitGranule);
+    const int32_t granules = std::max(1, g1 - g0);
+    int32_t splits = 1;
+    if (t.one_token) {
+      if (decode_splits > 0)
+        splits = std::min(decode_splits, granules);
+      else
+        splits = std::min(auto_splits, std::max(1, granules / 2));
+    }
+    int32_t part_row = -1;
+    if (splits > 1) {
+      part_row = n_split_rows;
+      n_split_rows += t.q_count;
+      max_splits = std::max(max_splits, splits);
+    }
+    for (int32_t h = 0; h < hkv; ++h) {
+      for (int32_t k = 0; k < splits; ++k) {
+        WorkItem it;
+        it.req = t.req;
+        it.kv_head = h;
+        it.q_begin = t.q_begin;
+        it.q_count = t.q_count;
+        if (splits == 1) {
+          it.kv_begin = t.kv_lo;
+          it.kv_end = t.kv_hi;
+        } else {
+          const int32_t ga = g0 + int32_t(int64_t(k) * granules / splits);
+          const int32_t gb = g0 + int32_t(int64_t(k + 1) * granules / splits);
+          it.kv_begin = std::max(t.kv_lo, ga * kSplitGranule);
+          it.kv_end = std::min(t.kv_hi, gb * kSplitGranule);
+        }
+        it.split = k;
+        it.part_row = part_row;
+        items.push_back(it);
+      }
+    }
+    if (splits > 1) {
+      // token indices are global: qo_indptr[req] + q_begin + i
+      for (int32_t i = 0; i < t.q_count; ++i) {
+        split_rows.push_back(qo_start[t.req] + t.q_begin + i);
+        split_rows.push_back(splits);
+      }
+    }
+  }
+
+  // Longest work first, so the long items start early and short ones fill the
+  // tail. An item's time grows with its key range times its live 32-row waves.
+  auto cost = [group](const WorkItem& a) {
+    return int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
+  };
+  std::stable_sort(items.begin(), items.end(),
+                   [&](const WorkItem& a, const WorkItem& b) { return cost(a) > cost(b); });
+
+  const int32_t n_items = int32_t(items.size());
+  const MetaLayout lay = meta_layout(batch, n_items, n_split_rows);
+  if (meta_bytes_out) *meta_bytes_out = lay.total;
+
+  if (plan) {
+    std::memset(plan, 0, sizeof(*plan));
+    plan->batch = batch;
+    plan->total_q = int32_t(total_q);
+    plan->max_q_len = max_q;
+    plan->max_kv_len = max_kv;
+    plan->n_items = n_items;
+    plan->n_split_rows = n_split_rows;
+    plan->max_splits = max_splits;
+    plan->window = window;
+    plan->shape = *shape;
+    plan->workspace_bytes = workspace_bytes(n_split_rows, hq, max_splits, shape->head_dim);
+  }
+
+  if (meta_host) {
+    if (meta_host_bytes < lay.total)
+      return set_error(PKV_ERR_WORKSPACE, "meta_host holds %zu bytes, %zu needed", meta_host_bytes, lay.total);
+    char* base = static_cast<char*>(meta_host);
+    std::memset(base, 0, lay.total);
+    int32_t* qo = reinterpret_cast<int32_t*>(base + lay.qo_indptr);
+    int32_t* kv = reinterpret_cast<int32_t*>(base + lay.kv_indptr);
+    int32_t* pre = reinterpret_cast<int32_t*>(base + lay.prefix_lens);
+    qo[0] = 0;
+    kv[0] = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      qo[b + 1] = qo[b] + chunk_lens[b];
+      kv[b + 1] = kv[b] + prefix_lens[b] + chunk_lens[b];
+      pre[b] = prefix_lens[b];
+    }
+    if (n_items) std::memcpy(base + lay.items, items.data(), sizeof(WorkItem) * items.size());
+    if (n_split_rows) std::memcpy(base + lay.split_rows, split_rows.data(), sizeof(int32_t) * split_rows.size());
+  }
+  return PKV_OK;
+}
+
+}  // namespace pkv

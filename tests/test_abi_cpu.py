@@ -1,0 +1,196 @@
+"""CPU-only checks of the C ABI library: it loads, exports every function that
+include/pkv.h declares, plans steps bit-exactly on the host, and rejects bad
+arguments with the documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_chunked_prefill_amd as pkv
+import workloads as wl
+from paged_chunked_prefill_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_abi.EXPORTS), names
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_header_layout():
+    # pkv_shape: 6 int32; pkv_plan: 8 int32 + shape + size_t + 6 pointers
+    assert ctypes.sizeof(pkv.PkvShape) == 24
+    assert ctypes.sizeof(pkv.PkvPlan) == 8 * 4 + 24 + 8 + 6 * 8
+
+
+def shape(hq=32, hkv=8, d=128, ps=16, pages=4096, dtype="bf16"):
+    return pkv.make_shape(hq, hkv, d, ps, pages, dtype)
+
+
+def test_indptrs_bit_exact():
+    w = wl.config2()
+    p = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape())
+    h = p.host_sections()
+    qo, kv = oracle.extend_metadata(w.prefix_lens, w.chunk_lens)
+    assert np.array_equal(h["qo_indptr"], qo) and np.array_equal(h["kv_indptr"], kv)
+    assert np.array_equal(h["prefix_lens"], w.prefix_lens)
+    assert p.plan.total_q == 705 and p.plan.max_q_len == 512 and p.plan.max_kv_len == 1537
+    assert p.plan.n_items == 184            # (1 + 2 + 4 + 16) tiles x 8 KV heads
+    assert h["status"][0] == 0
+
+
+def coverage(p, P, L, hq, hkv, window):
+    """Every (token, query head) row is covered by exactly one tile item, or by
+    S split items whose key ranges partition the row's visible range."""
+    h = p.host_sections()
+    items = h["items"]
+    G = hq // hkv
+    qo, _ = oracle.extend_metadata(P, L)
+    seen = {}
+    for it in items:
+        b, hk = int(it["req"]), int(it["kv_head"])
+        for t in range(int(it["q_begin"]), int(it["q_begin"]) + int(it["q_count"])):
+            for g in range(G):
+                seen.setdefault((int(qo[b]) + t, hk * G + g), []).append(it)
+    split_tok = {int(r[0]): int(r[1]) for r in h["split_rows"]}
+    assert len(seen) == int(np.sum(L)) * hq
+    for (tok, head), its in seen.items():
+        b = int(np.searchsorted(qo, tok, side="right") - 1)
+        i = tok - int(qo[b])
+        pos = int(P[b]) + i
+        lo, hi = oracle.visible_range(pos, window)
+        if len(its) == 1:
+            assert its[0]["part_row"] == -1
+            assert its[0]["kv_begin"] <= lo and its[0]["kv_end"] >= hi
+        else:
+            assert split_tok[tok] == len(its)
+            rng = sorted((int(x["kv_begin"]), int(x["kv_end"])) for x in its)
+            assert sorted(int(x["split"]) for x in its) == list(range(len(its)))
+            assert rng[0][0] <= lo and rng[-1][1] >= hi
+            for a, c in zip(rng, rng[1:]):
+                assert a[1] == c[0]          # contiguous, disjoint
+            assert all(a < c for a, c in rng)  # no empty split
+
+
+@pytest.mark.parametrize("cfg", ["config2", "config5", "config4", "mixed"])
+def test_work_list_covers_every_row_once(cfg):
+    if cfg == "config2":
+        w, s, splits = wl.config2(), shape(), 0
+    elif cfg == "config5":
+        w = wl.config5()
+        s, splits = shape(64, 8, 128, 16, w.num_pages), 8
+    elif cfg == "config4":
+        w = wl.config4(mid_page=True)
+        s, splits = shape(32, 8, 128, 16, w.num_pages), 0
+    else:
+        P = np.array([0, 5000, 17, 1, 0, 3], np.int32)
+        L = np.array([300, 1, 1, 0, 1, 64], np.int32)
+        w = wl.Workload("mixed", 7, "bf16", 12, 4, 64, 16, 1024, 0, P, L, wl.shuffled_page_table(7, 1024, P + L, 16))
+        s, splits = shape(12, 4, 64, 16, 1024), 0
+    p = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, s, w.window, splits)
+    coverage(p, w.prefix_lens, w.chunk_lens, s.num_q_heads, s.num_kv_heads, w.window)
+
+
+def test_config5_split_plan():
+    w = wl.config5()
+    p = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape(64, 8, 128, 16, w.num_pages), 0, 8)
+    assert p.plan.n_items == 64 * 8 * 8 + 2 * 8 * (2048 // 16)
+    assert p.plan.n_split_rows == 64 and p.plan.max_splits == 8
+    assert p.plan.workspace_bytes >= 64 * 64 * 8 * (128 + 2) * 4
+    mb, wb = pkv.extend_metadata_size(w.prefix_lens, w.chunk_lens, shape(64, 8, 128, 16, w.num_pages), 0, 8)
+    assert wb == p.plan.workspace_bytes and mb == p.meta_host.size
+
+
+def test_window_ranges_are_tight():
+    P, L = np.array([6000], np.int32), np.array([1000], np.int32)
+    p = pkv.build_extend_metadata(P, L, shape(32, 8, 128, 16, 1000), 4096, 0)
+    for it in p.host_sections()["items"]:
+        first = 6000 + int(it["q_begin"])
+        last = first + int(it["q_count"]) - 1
+        assert it["kv_begin"] == first - 4096 + 1 and it["kv_end"] == last + 1
+
+
+def status_of(fn):
+    try:
+        fn()
+    except pkv.PkvError as e:
+        return e.status
+    return 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=[-1], L=[4]), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(P=[0], L=[-4]), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(P=[2**31 - 2], L=[4]), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(P=[2**30, 2**30], L=[4, 4]), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(s=dict(hq=30, hkv=8)), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(s=dict(hkv=0)), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(s=dict(ps=0)), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(s=dict(pages=0)), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(s=dict(d=96)), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(s=dict(d=256)), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(s=dict(dtype=7)), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(s=dict(hq=256, hkv=1)), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(splits=33), pkv.PKV_ERR_INVALID_ARGUMENT),
+    (dict(splits=-1), pkv.PKV_ERR_INVALID_ARGUMENT),
+])
+def test_invalid_arguments_rejected(kw, status):
+    P = kw.get("P", [3, 5])
+    L = kw.get("L", [1, 2])
+    s = shape(**kw.get("s", {}))
+    assert status_of(lambda: pkv.build_extend_metadata(P, L, s, 0, kw.get("splits", 0))) == status
+    assert pkv.lib().pkv_last_error().decode()
+
+
+def test_batch_zero_and_small_buffers_rejected():
+    lib = pkv.lib()
+    s = shape()
+    plan = pkv.PkvPlan()
+    P = np.array([1], np.int32)
+    L = np.array([1], np.int32)
+    buf = np.zeros(16, np.uint8)
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    assert lib.build_extend_metadata(0, vp(P), vp(L), ctypes.byref(s), 0, 0, vp(buf), 16, None, 0,
+                                     ctypes.byref(plan), None) == pkv.PKV_ERR_INVALID_ARGUMENT
+    assert lib.build_extend_metadata(1, vp(P), vp(L), ctypes.byref(s), 0, 0, vp(buf), 16, None, 0,
+                                     ctypes.byref(plan), None) == pkv.PKV_ERR_WORKSPACE
+    assert lib.build_extend_metadata(1, None, vp(L), ctypes.byref(s), 0, 0, vp(buf), 16, None, 0,
+                                     ctypes.byref(plan), None) == pkv.PKV_ERR_INVALID_ARGUMENT
+
+
+def test_host_only_plan_cannot_launch():
+    """A host-only plan has no device metadata: the launches refuse it before any HIP call."""
+    lib = pkv.lib()
+    s = shape()
+    p = pkv.build_extend_metadata([3], [2], s)
+    dummy = ctypes.c_void_p(0x1000)
+    st = lib.pkv_append(dummy, dummy, dummy, dummy, dummy, 4, None, ctypes.byref(p.plan), ctypes.byref(s), None)
+    assert st == pkv.PKV_ERR_INVALID_ARGUMENT
+    st = lib.paged_extend_attn(dummy, dummy, dummy, dummy, 4, None, None, None, None, 0, 0.0, ctypes.byref(p.plan),
+                               ctypes.byref(s), dummy, None, 0, None)
+    assert st == pkv.PKV_ERR_INVALID_ARGUMENT
+    assert "device metadata" in lib.pkv_last_error().decode()
+
+
+def test_auto_splits_follow_the_cu_heuristic():
+    # 4 one-token rows with long KV and 8 KV heads: 32 base items -> ceil(512/32) = 16 splits
+    P = np.full(4, 20000, np.int32)
+    L = np.ones(4, np.int32)
+    p = pkv.build_extend_metadata(P, L, shape(32, 8, 128, 16, 8000), 0, 0)
+    assert p.plan.max_splits == 16 and p.plan.n_items == 4 * 8 * 16
+    # one-token rows with very short KV are not split below 2 blocks of 64 keys per split
+    p = pkv.build_extend_metadata([100], [1], shape(32, 8, 128, 16, 8000), 0, 0)
+    assert p.plan.max_splits == 1

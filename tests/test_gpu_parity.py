@@ -1,0 +1,301 @@
+"""Parity of the HIP path (called through the C ABI via the Python binding)
+with the CPU oracle, on the seeded workloads: element by element at sizes the
+oracle finishes in seconds, on sampled rows at full size.
+
+Bar: bf16 |gpu - ref| <= 2e-2 + 1e-2 |ref|, fp32 <= 1e-5 + 1e-5 |ref|, against
+the fp32 oracle; page-table and indptr handling bit-exact (append compared
+bytewise, NaN canaries included)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from pkv_testlib import assert_parity, oracle_out, oracle_pools
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_chunked_prefill_amd as pkv
+    from gpu_harness import (DeviceCache, chunked_prefill, from_dev, prefill_and_attend, run_attention, shape_of,
+                             upload_q, values_of)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    assert pkv.device_supported(torch.cuda.current_device()), "not a gfx950 device"
+
+
+def report(name, rep):
+    print(f"[parity] {name}: max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}", flush=True)
+
+
+def check(name, out, ref, dtype):
+    got = values_of(out) if isinstance(out, torch.Tensor) else out
+    assert not np.isnan(got).any(), f"{name}: NaN in output"
+    report(name, assert_parity(got, ref, dtype, name))
+
+
+def oracle_request_rows(w: wl.Workload, b: int, rows, dtype=np.float32):
+    """Oracle output of chunk rows `rows` (0-based within request b's chunk) of
+    one request, from a compact pool holding only that request's pages."""
+    P, L = int(w.prefix_lens[b]), int(w.chunk_lens[b])
+    n = P + L
+    npg = (n + w.page_size - 1) // w.page_size
+    one = wl.Workload(w.name, w.config_id, w.dtype, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, npg,
+                      w.window, np.array([P], np.int32), np.array([L], np.int32),
+                      np.arange(npg, dtype=np.int32)[None], request_ids=np.array([w.rid(b)]),
+                      data_scale=w.data_scale, zero_q=w.zero_q, ramp_v=w.ramp_v, ramp_v_step=w.ramp_v_step)
+    k, v = w.kv_seq(b, storage=True)
+    kp, vp = one.empty_pool(), one.empty_pool()
+    kp, vp = oracle.append_kv(kp, vp, k, v, one.page_table, [0], [n])
+    return oracle_out(one, (kp, vp), dtype=dtype, rows=list(rows))[list(rows)]
+
+
+# ---------------------------------------------------------------------------
+# append (bit-exact)
+# ---------------------------------------------------------------------------
+
+def pools_equal_bytes(cache, pools):
+    for dev, ref in zip((cache.k_pool, cache.v_pool), pools):
+        got = from_dev(dev)
+        a = got.view(np.uint16 if got.dtype == np.uint16 else np.uint32)
+        b = ref.view(np.uint16 if ref.dtype == np.uint16 else np.uint32)
+        assert np.array_equal(a, b), f"pool bytes differ at {np.argwhere(a != b)[:5].tolist()}"
+
+
+def test_canary_bits_match():
+    t = torch.full((4,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert (from_dev(t) == wl.nan_fill("bf16")).all()
+
+
+def test_append_bitexact_ragged():
+    w = wl.config2()
+    cache = DeviceCache(w)
+    cache.fill_prefix(w)
+    cache.append_step(w)
+    torch.cuda.synchronize()
+    pools_equal_bytes(cache, oracle_pools(w))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_append_bitexact_mid_page(dtype):
+    P = np.array([6001 + 2 * b for b in range(8)], np.int32)
+    L = np.array([3, 17, 1, 0, 33, 16, 2, 64], np.int32)
+    pt = wl.shuffled_page_table(40, 4096, P + L, 16)
+    w = wl.Workload("mid-page", 40, dtype, 8, 2, 64, 16, 4096, 0, P, L, pt)
+    cache = DeviceCache(w)
+    cache.fill_prefix(w)
+    cache.append_step(w)
+    torch.cuda.synchronize()
+    pools_equal_bytes(cache, oracle_pools(w))
+
+
+# ---------------------------------------------------------------------------
+# config 1 (fp32): parity at 1e-5, zero-score closed form, partitions
+# ---------------------------------------------------------------------------
+
+def test_config1_fp32():
+    w = wl.config1()
+    out, cache, plan = prefill_and_attend(w)
+    check("config1", out, oracle_out(w, oracle_pools(w)), "fp32")
+
+
+@pytest.mark.parametrize("chunks", [[64], [48, 16], [16, 16, 16, 16], [1] * 64, [15, 33, 16]])
+def test_config1_zero_score_exact(chunks):
+    w = wl.config1(zero_score=True).with_lengths([0], [64])
+    out, _ = chunked_prefill(w, chunks)
+    t = np.arange(64, dtype=np.float32)
+    want = np.broadcast_to(((t + 2) / 2)[:, None, None], (64, 2, 64))
+    assert np.array_equal(values_of(out), want)
+
+
+@pytest.mark.parametrize("chunks", [[16, 16, 16, 16], [1] * 64, [48, 16]])
+def test_config1_partitions_match_full_prefill(chunks):
+    w = wl.config1().with_lengths([0], [64])
+    full, _ = chunked_prefill(w, [64])
+    part, _ = chunked_prefill(w, chunks)
+    ref = oracle_out(w, oracle_pools(w))
+    check(f"config1 full", full, ref, "fp32")
+    check(f"config1 {chunks[:3]}..", part, ref, "fp32")
+    bitwise = torch.equal(full, part)
+    print(f"[parity] config1 partition {len(chunks)} chunks bitwise-equal to full prefill: {bitwise}")
+
+
+def test_zero_score_page_literal_bf16():
+    """The PR's regression numbers on the bf16 path: [1,2,3,4] across two chunks of two."""
+    w = wl.Workload("literal", 41, "bf16", 8, 8, 128, 2, 8, 0, np.array([0], np.int32), np.array([4], np.int32),
+                    np.array([[5, 2, 7, 0]], np.int32), zero_q=True, ramp_v=True, ramp_v_step=2.0)
+    out, _ = chunked_prefill(w, [2, 2])
+    assert np.array_equal(values_of(out)[:, 0, 0], np.array([1, 2, 3, 4], np.float32))
+    assert np.array_equal(values_of(out), np.broadcast_to(np.array([1, 2, 3, 4], np.float32)[:, None, None],
+                                                          (4, 8, 128)))
+
+
+# ---------------------------------------------------------------------------
+# config 2 (ragged bf16, NaN canaries)
+# ---------------------------------------------------------------------------
+
+def test_config2_ragged():
+    w = wl.config2()
+    out, cache, plan = prefill_and_attend(w)
+    check("config2", out, oracle_out(w, oracle_pools(w)), "bf16")
+    assert pkv.read_status(plan) == 0
+
+
+def test_page_permutation_invariance_bitwise():
+    w = wl.config2()
+    out1, _, _ = prefill_and_attend(w)
+    pt2 = wl.shuffled_page_table(999, w.num_pages, w.kv_lens, w.page_size)
+    w2 = wl.Workload(**{**w.__dict__, "page_table": pt2})
+    out2, _, _ = prefill_and_attend(w2)
+    assert torch.equal(out1, out2)
+
+
+# ---------------------------------------------------------------------------
+# config 3 (long prompt, chunk budgets)
+# ---------------------------------------------------------------------------
+
+_REF3 = {}
+
+
+def ref3(prompt):
+    if prompt not in _REF3:
+        w = wl.config3(prompt)
+        _REF3[prompt] = oracle_out(w, oracle_pools(w))
+    return _REF3[prompt]
+
+
+@pytest.mark.parametrize("prompt", [4097, 8193])
+@pytest.mark.parametrize("budget,first", [(2048, None), (512, None), (128, None), (512, 511), (None, None)])
+def test_config3_chunked_matches_full(prompt, budget, first):
+    w = wl.config3(prompt)
+    chunks = [prompt] if budget is None else wl.chunk_partition(prompt, budget, first)
+    out, _ = chunked_prefill(w, chunks)
+    check(f"config3 {prompt} budget={budget} first={first}", out, ref3(prompt), "bf16")
+
+
+# ---------------------------------------------------------------------------
+# config 4 (sliding window)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mid_page", [False, True])
+def test_config4_window(mid_page):
+    w = wl.config4(mid_page)
+    out, cache, plan = prefill_and_attend(w)
+    got = values_of(out)
+    assert not np.isnan(got).any()
+    rows = [0, 1, 2, 15, 16, 17, 63, 64, 500, 998, 999]
+    for b in (0, 3, 7):
+        ref = oracle_request_rows(w, b, rows)
+        base = int(np.sum(w.chunk_lens[:b]))
+        check(f"config4 mid_page={mid_page} req {b}", got[[base + r for r in rows]], ref, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# config 5 (mixed decode + prefill, split-KV)
+# ---------------------------------------------------------------------------
+
+def test_config5_mixed_full_size():
+    w = wl.config5()
+    out, cache, plan = prefill_and_attend(w)
+    assert plan.plan.n_split_rows == 64 and plan.plan.max_splits == 8
+    got = values_of(out)
+    assert not np.isnan(got).any()
+    for b in list(range(0, 64, 9)) + [63]:
+        check(f"config5 decode req {b}", got[[b]], oracle_request_rows(w, b, [0]), "bf16")
+    for b in (64, 65):
+        rows = [0, 1, 17, 1023, 2046, 2047]
+        base = 64 + (b - 64) * 2048
+        check(f"config5 prefill req {b}", got[[base + r for r in rows]], oracle_request_rows(w, b, rows), "bf16")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 0])
+def test_decode_splits_agree(splits):
+    w = wl.config5(decode_only=True).subset(range(6))
+    out, _, plan = prefill_and_attend(w, decode_splits=splits)
+    got = values_of(out)
+    for b in range(6):
+        check(f"decode splits={splits} req {b}", got[[b]], oracle_request_rows(w, b, [0]), "bf16")
+
+
+def test_split_zero_score_exact():
+    P = np.array([999, 2047, 77], np.int32)
+    L = np.ones(3, np.int32)
+    w = wl.Workload("zs-split", 42, "fp32", 4, 2, 64, 16, 512, 0, P, L,
+                    wl.shuffled_page_table(42, 512, P + L, 16), zero_q=True, ramp_v=True, decode_splits=8)
+    out, _, plan = prefill_and_attend(w)
+    assert plan.plan.n_split_rows == 3
+    want = (P.astype(np.float32) + 2) / 2          # mean of 1..N
+    assert np.array_equal(values_of(out)[:, 0, 0], want)
+
+
+# ---------------------------------------------------------------------------
+# edge cases and variants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D,hq,hkv,ps,window", [
+    ("bf16", 64, 4, 4, 1, 0), ("bf16", 128, 6, 2, 3, 0), ("bf16", 64, 12, 4, 7, 33), ("fp32", 128, 4, 1, 16, 0),
+    ("fp32", 64, 3, 3, 5, 10), ("bf16", 128, 16, 1, 64, 100)])
+def test_variants(dtype, D, hq, hkv, ps, window):
+    P = np.array([0, 37, 0, 130, 64], np.int32)
+    L = np.array([70, 0, 1, 45, 129], np.int32)
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 5
+    w = wl.Workload(f"variant", 43, dtype, hq, hkv, D, ps, pages, window, P, L,
+                    wl.shuffled_page_table(43, pages, P + L, ps))
+    out, _, _ = prefill_and_attend(w)
+    check(f"variant {dtype} D={D} {hq}/{hkv} ps={ps} W={window}", out, oracle_out(w, oracle_pools(w)), dtype)
+
+
+def test_req_pool_indices_and_scale():
+    w = wl.config2()
+    out_ref, cache, plan = prefill_and_attend(w, decode_splits=0)
+    # the same requests stored in permuted page-table rows
+    perm = np.array([2, 0, 3, 1], np.int32)
+    pt_rows = np.full((4, w.page_table.shape[1]), -1, np.int32)
+    pt_rows[perm] = w.page_table
+    rpi = torch.from_numpy(perm).cuda()
+    table = torch.from_numpy(pt_rows).cuda()
+    q = upload_q(w)
+    out = pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, table, plan, req_pool_indices=rpi)
+    assert torch.equal(out, out_ref)
+    out_s = pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, sm_scale=0.3)
+    check("config2 sm_scale=0.3", out_s, oracle_out(w, oracle_pools(w), sm_scale=0.3), "bf16")
+
+
+def test_window_one_is_own_value_bitwise():
+    P, L = np.array([40], np.int32), np.array([24], np.int32)
+    w = wl.Workload("w1", 44, "bf16", 8, 2, 128, 16, 8, 1, P, L, wl.shuffled_page_table(44, 8, P + L, 16))
+    out, _, _ = prefill_and_attend(w)
+    v = w.kv_seq(0, storage=True)[1][40:64]
+    assert np.array_equal(from_dev(out), np.repeat(v, 4, axis=1))
+
+
+def test_bad_page_id_is_flagged_not_read():
+    P, L = np.array([32], np.int32), np.array([32], np.int32)
+    w = wl.Workload("bad", 45, "bf16", 8, 2, 128, 16, 16, 0, P, L, wl.shuffled_page_table(45, 16, P + L, 16))
+    cache = DeviceCache(w)
+    cache.fill_prefix(w)
+    plan = cache.append_step(w)
+    torch.cuda.synchronize()
+    assert pkv.read_status(plan) == 0
+    bad = w.page_table.copy()
+    bad[0, 1] = 10_000                        # out of the pool: must never be dereferenced
+    table = torch.from_numpy(bad).cuda()
+    out = pkv.paged_extend_attn(upload_q(w), cache.k_pool, cache.v_pool, table, plan)
+    torch.cuda.synchronize()
+    assert pkv.read_status(plan) == pkv.PKV_STATUS_BAD_PAGE
+    assert not torch.isnan(out.float()).any()
+
+
+def test_empty_chunks_only():
+    P, L = np.array([5, 9], np.int32), np.array([0, 0], np.int32)
+    w = wl.Workload("empty", 46, "bf16", 4, 2, 64, 16, 4, 0, P, L, wl.shuffled_page_table(46, 4, P + L, 16))
+    cache = DeviceCache(w)
+    plan = cache.append_step(w)
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4, 64)

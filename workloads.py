@@ -25,12 +25,24 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
 Q_STREAM, K_STREAM, V_STREAM, PAGE_STREAM, LEN_STREAM = 0, 1, 2, 3, 4
 ROW_BLOCK = 256
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
 
 
 def rng(config_id: int, stream: int, request: int = 0) -> np.random.Generator:
@@ -122,82 +134,83 @@ class Workload:
         return int(self.request_ids[b]) if self.request_ids is not None else b
 
     # -- per-request values (float32, exactly representable in the storage dtype)
-    def _normal_rows(self, stream: int, b: int, lo: int, hi: int, heads: int) -> np.ndarray:
-        """N(0,1) rows lo..hi-1 of one request; rows are drawn in blocks of
-        ``ROW_BLOCK`` positions, each block from its own seeded stream, so any
-        range can be regenerated without drawing the rows before it."""
-        out = np.empty((max(0, hi - lo), heads, self.head_dim), np.float32)
+    def _normal_rows(self, stream: int, b: int, lo: int, hi: int, heads: int, storage: bool) -> np.ndarray:
+        """N(0,1) x data_scale rows lo..hi-1 of one request, rounded to the storage
+        dtype; returned as storage (bf16 bits / float32) or as the float32 values
+        those bits hold. Rows are drawn in blocks of ``ROW_BLOCK`` positions, each
+        block from its own seeded stream, so any range can be regenerated without
+        drawing the rows before it (and blocks can be drawn on several threads
+        with the same result)."""
+        out_dt = storage_np_dtype(self.dtype) if storage else np.float32
+        out = np.empty((max(0, hi - lo), heads, self.head_dim), out_dt)
         rid = self.rid(b)
-        for blk in range(lo // ROW_BLOCK, (hi + ROW_BLOCK - 1) // ROW_BLOCK):
+        scale = np.float32(self.data_scale)
+
+        def fill(blk):
             b0 = blk * ROW_BLOCK
             g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
                 [int(self.config_id), int(stream), rid, blk])))
-            rows = g.standard_normal((ROW_BLOCK, heads, self.head_dim), dtype=np.float32)
             s, e = max(lo, b0), min(hi, b0 + ROW_BLOCK)
-            out[s - lo:e - lo] = rows[s - b0:e - b0]
+            rows = g.standard_normal((ROW_BLOCK, heads, self.head_dim), dtype=np.float32)[s - b0:e - b0]
+            if self.data_scale != 1.0:
+                rows = rows * scale
+            st = to_storage(rows, self.dtype)
+            out[s - lo:e - lo] = st if storage else values(st, self.dtype)
+
+        blocks = range(lo // ROW_BLOCK, (hi + ROW_BLOCK - 1) // ROW_BLOCK)
+        if len(blocks) > 4:
+            list(_pool().map(fill, blocks))
+        else:
+            for blk in blocks:
+                fill(blk)
         return out
 
-    def kv_seq(self, b: int, upto: Optional[int] = None, start: int = 0) -> Tuple[np.ndarray, np.ndarray]:
-        """K/V of request b for positions start..upto-1 (default 0..N_b-1)."""
+    def kv_seq(self, b: int, upto: Optional[int] = None, start: int = 0,
+               storage: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+        """K/V of request b for positions start..upto-1 (default 0..N_b-1), as
+        float32 values (default) or in storage format."""
         n = int(self.kv_lens[b]) if upto is None else int(upto)
-        k = self._normal_rows(K_STREAM, b, start, n, self.num_kv_heads)
+        k = self._normal_rows(K_STREAM, b, start, n, self.num_kv_heads, storage)
         if self.ramp_v:
             t = np.arange(start, n, dtype=np.float32) * np.float32(self.ramp_v_step) + np.float32(1)
             v = np.broadcast_to(t[:, None, None], k.shape).astype(np.float32)
+            v = to_storage(v, self.dtype) if storage else values(to_storage(v, self.dtype), self.dtype)
         else:
-            v = self._normal_rows(V_STREAM, b, start, n, self.num_kv_heads)
-        if self.data_scale != 1.0:
-            k = k * np.float32(self.data_scale)
-            if not self.ramp_v:
-                v = v * np.float32(self.data_scale)
-        return values(to_storage(k, self.dtype), self.dtype), values(to_storage(v, self.dtype), self.dtype)
+            v = self._normal_rows(V_STREAM, b, start, n, self.num_kv_heads, storage)
+        return k, v
 
-    def q_rows(self, b: int, lo: int, hi: int) -> np.ndarray:
+    def q_rows(self, b: int, lo: int, hi: int, storage: bool = False) -> np.ndarray:
         """Queries of request b at positions lo..hi-1. A position's query does not
         depend on how the prompt was partitioned into chunks."""
         if self.zero_q:
-            return np.zeros((max(0, hi - lo), self.num_q_heads, self.head_dim), np.float32)
-        q = self._normal_rows(Q_STREAM, b, lo, hi, self.num_q_heads)
-        if self.data_scale != 1.0:
-            q = q * np.float32(self.data_scale)
-        return values(to_storage(q, self.dtype), self.dtype)
+            z = np.zeros((max(0, hi - lo), self.num_q_heads, self.head_dim), np.float32)
+            return to_storage(z, self.dtype) if storage else z
+        return self._normal_rows(Q_STREAM, b, lo, hi, self.num_q_heads, storage)
 
-    def q_chunk(self, b: int) -> np.ndarray:
-        return self.q_rows(b, int(self.prefix_lens[b]), int(self.kv_lens[b]))
+    def q_chunk(self, b: int, storage: bool = False) -> np.ndarray:
+        return self.q_rows(b, int(self.prefix_lens[b]), int(self.kv_lens[b]), storage)
 
-    def chunk_kv(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
-        return self.kv_seq(b, start=int(self.prefix_lens[b]))
+    def chunk_kv(self, b: int, storage: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+        return self.kv_seq(b, start=int(self.prefix_lens[b]), storage=storage)
 
     # -- whole-batch arrays, in storage format, for handing to either side
+    def _cat(self, parts, heads):
+        if parts:
+            return np.concatenate(parts, 0)
+        return np.zeros((0, heads, self.head_dim), storage_np_dtype(self.dtype))
+
     def q_all(self) -> np.ndarray:
-        parts = [self.q_chunk(b) for b in range(self.batch)]
-        x = np.concatenate(parts, 0) if parts else np.zeros((0, self.num_q_heads, self.head_dim), np.float32)
-        return to_storage(x, self.dtype)
+        return self._cat([self.q_chunk(b, storage=True) for b in range(self.batch)], self.num_q_heads)
 
     def new_kv_all(self) -> Tuple[np.ndarray, np.ndarray]:
-        ks, vs = [], []
-        for b in range(self.batch):
-            k, v = self.chunk_kv(b)
-            ks.append(k)
-            vs.append(v)
-        shp = (0, self.num_kv_heads, self.head_dim)
-        k = np.concatenate(ks, 0) if ks else np.zeros(shp, np.float32)
-        v = np.concatenate(vs, 0) if vs else np.zeros(shp, np.float32)
-        return to_storage(k, self.dtype), to_storage(v, self.dtype)
+        kv = [self.chunk_kv(b, storage=True) for b in range(self.batch)]
+        return (self._cat([k for k, _ in kv], self.num_kv_heads), self._cat([v for _, v in kv], self.num_kv_heads))
 
     def prefix_kv_all(self) -> Tuple[np.ndarray, np.ndarray]:
         """K/V of every request's cached prefix, concatenated in request order
         (what an earlier step would have appended)."""
-        ks, vs = [], []
-        for b in range(self.batch):
-            p = int(self.prefix_lens[b])
-            k, v = self.kv_seq(b, upto=p)
-            ks.append(k)
-            vs.append(v)
-        shp = (0, self.num_kv_heads, self.head_dim)
-        k = np.concatenate(ks, 0) if ks else np.zeros(shp, np.float32)
-        v = np.concatenate(vs, 0) if vs else np.zeros(shp, np.float32)
-        return to_storage(k, self.dtype), to_storage(v, self.dtype)
+        kv = [self.kv_seq(b, upto=int(self.prefix_lens[b]), storage=True) for b in range(self.batch)]
+        return (self._cat([k for k, _ in kv], self.num_kv_heads), self._cat([v for _, v in kv], self.num_kv_heads))
 
     def empty_pool(self) -> np.ndarray:
         shape = (self.num_pages, self.page_size, self.num_kv_heads, self.head_dim)
