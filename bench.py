@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged extend-attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: for every batch
+of the workload, build the step metadata (host planner + its copy to the
+device), append the chunk's K/V into the pages, run the extend attention
+(plus the split combine when the plan has split rows). The default workload
+is a 4097-token prompt prefilled to completion under a 512-token chunk budget
+(9 chunks; 16 query / 4 KV heads, head_dim 128, 64-token pages, bf16).
+
+Prints ONE JSON line. `value` is extend-attention TFLOP/s over the step
+(algorithmic FLOPs: 4*D*Hq per visible (query, key) pair); `tokens_per_s`
+counts query tokens. `roofline` is for the attention kernel, timed with
+events around each launch on the launch stream; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+METRIC = "extend-attn TFLOP/s + % bf16 MFMA peak (4097-tok prompt, 512 chunk), tokens/s"
+MFMA_PEAK_BF16 = 2500.0      # TFLOP/s, MI355X dense bf16
+MFMA_PEAK_FP32 = 157.3       # TFLOP/s, MI355X fp32 matrix (vector figure as stated for the chip)
+HBM_PEAK = 8000.0            # GB/s
+
+
+# ---------------------------------------------------------------------------
+# workloads: a list of batches run in order against one cache
+# ---------------------------------------------------------------------------
+
+def workload(name):
+    import workloads as wl
+    if name.startswith("prompt"):
+        # promptN_chunkB
+        n, b = name[len("prompt"):].split("_chunk")
+        w = wl.config3(int(n))
+        chunks = wl.chunk_partition(int(n), int(b))
+        desc = (f"{n}-token prompt prefilled in {len(chunks)} chunks of <= {b} tokens; 16 query / 4 KV heads, "
+                f"head_dim 128, page_size 64, bf16")
+        return w, wl.chunked_steps(w, chunks), False, desc
+    if name == "ragged4":
+        w = wl.config2()
+        return w, [w], True, "ragged batch P={0,100,513,1025} L={1,64,128,512}; 32/8 heads, D=128, ps=16, bf16"
+    if name == "window8":
+        w = wl.config4()
+        return w, [w], True, "8 x (6000 cached + 1000 new), window 4096; 32/8 heads, D=128, ps=16, bf16"
+    if name == "mixed":
+        w = wl.config5()
+        return w, [w], True, ("64 one-token rows (KV 2048..32768, 8 splits) + 2 x (16384 + 2048) prefill rows; "
+                              "64/8 heads, D=128, ps=16, bf16")
+    if name == "decode64":
+        w = wl.config5(decode_only=True)
+        return w, [w], True, "64 one-token rows (KV 2048..32768, 8 splits); 64/8 heads, D=128, ps=16, bf16"
+    if name == "prefill2":
+        w = wl.config5(prefill_only=True)
+        return w, [w], True, "2 x (16384 cached + 2048 new); 64/8 heads, D=128, ps=16, bf16"
+    raise SystemExit(f"unknown workload {name}")
+
+
+def visible_pairs(P, L, window):
+    import numpy as np
+    tot = 0
+    for p, l in zip(P, L):
+        pos = np.arange(int(p), int(p) + int(l), dtype=np.int64)
+        vis = pos + 1
+        if window > 0:
+            vis = np.minimum(vis, window)
+        tot += int(vis.sum())
+    return tot
+
+
+def kv_span_tokens(P, L, window):
+    tot = 0
+    for p, l in zip(P, L):
+        lo = 0 if window <= 0 else max(0, int(p) - window + 1)
+        tot += int(p) + int(l) - lo
+    return tot
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prompt4097_chunk512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows for the CPU oracle sample (0: auto)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build is single-GPU only (paged extend attention on one MI355X); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_chunked_prefill_amd as pkv
+    from gpu_harness import DeviceCache, shape_of, to_dev, upload_q
+
+    torch.cuda.set_device(0)
+    if not pkv.device_supported(0):
+        raise SystemExit("device 0 is not gfx950")
+    lib = pkv.lib()
+    w, batches, prefill_prefix, desc = workload(args.workload)
+    shape = shape_of(w)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    t_setup = time.time()
+    cache = DeviceCache(w, dev)
+    if prefill_prefix:
+        cache.fill_prefix(w)
+    nsteps = args.warmup + args.steps
+
+    # per batch: device inputs, output, metadata buffers, pre-marshalled ctypes arguments
+    B = []
+    for bw in batches:
+        P = np.ascontiguousarray(bw.prefix_lens, np.int32)
+        L = np.ascontiguousarray(bw.chunk_lens, np.int32)
+        splits = bw.decode_splits
+        meta_bytes, ws_bytes = pkv.extend_metadata_size(P, L, shape, bw.window, splits)
+        kn, vn = cache._gather_new_kv(bw)
+        q = upload_q(bw, dev)
+        out = torch.empty_like(q)
+        meta_dev = torch.empty(meta_bytes, dtype=torch.uint8, device=dev)
+        hosts = [torch.empty(meta_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(nsteps)]
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        plan = pkv.PkvPlan()
+        b = dict(P=P, L=L, kn=kn, vn=vn, q=q, out=out, meta_dev=meta_dev, hosts=hosts, ws=ws, plan=plan,
+                 total_q=int(L.sum()), flops=4 * w.head_dim * w.num_q_heads * visible_pairs(P, L, bw.window),
+                 bytes=2 * (2 * int(L.sum()) * w.num_q_heads * w.head_dim +
+                            2 * w.num_kv_heads * w.head_dim * kv_span_tokens(P, L, bw.window)))
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        b["meta_args"] = [(len(L), P.ctypes.data_as(ctypes.c_void_p), L.ctypes.data_as(ctypes.c_void_p),
+                           ctypes.byref(shape), bw.window, splits, vp(h), meta_bytes, vp(meta_dev), meta_bytes,
+                           ctypes.byref(plan), sh) for h in hosts]
+        b["append_args"] = (vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
+                            cache.page_table.shape[1], None, ctypes.byref(plan), ctypes.byref(shape), sh)
+        b["attn_args"] = (vp(q), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table), cache.page_table.shape[1],
+                          None, None, None, None, bw.window, 0.0, ctypes.byref(plan), ctypes.byref(shape), vp(out),
+                          vp(ws), ws.numel(), sh)
+        B.append(b)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in B]
+          for _ in range(nsteps)]
+    build, append, attn = lib.build_extend_metadata, lib.pkv_append, lib.paged_extend_attn
+
+    def step(s):
+        for i, b in enumerate(B):
+            if build(*b["meta_args"][s]):
+                raise RuntimeError(lib.pkv_last_error().decode())
+            if append(*b["append_args"]):
+                raise RuntimeError(lib.pkv_last_error().decode())
+            ev[s][i][0].record(stream)
+            if attn(*b["attn_args"]):
+                raise RuntimeError(lib.pkv_last_error().decode())
+            ev[s][i][1].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, nsteps):
+        step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    attn_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.warmup, nsteps)) / args.steps
+               for i in range(len(B))]
+    flops = sum(b["flops"] for b in B)
+    hbm_bytes = sum(b["bytes"] for b in B)
+    tokens = sum(b["total_q"] for b in B)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    attn_total_ms = sum(attn_ms)
+    attn_tflops = flops / (attn_total_ms * 1e-3) / 1e12
+    attn_gbs = hbm_bytes / (attn_total_ms * 1e-3) / 1e9
+    n_launch = len(B)
+    decode_bound = args.workload == "decode64"
+    roofline = {
+        "kernel": f"extend_attn_{w.dtype}<{w.head_dim}>" + (" + combine_splits" if any(
+            b["plan"].n_split_rows for b in B) else ""),
+        "bound": "hbm" if decode_bound else "mfma",
+        "achieved": round(attn_gbs if decode_bound else attn_tflops, 3),
+        "peak": HBM_PEAK if decode_bound else (MFMA_PEAK_BF16 if w.dtype == "bf16" else MFMA_PEAK_FP32),
+        "unit": "GB/s" if decode_bound else "TFLOP/s",
+        "frac": None, "traffic": None,
+        "avg_launch_us": round(1e3 * attn_total_ms / n_launch, 3),
+        "launches_per_step": n_launch,
+        "algorithmic_per_launch": round((hbm_bytes if decode_bound else flops) / n_launch),
+    }
+    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+
+    # check the last step's outputs are finite (no canary NaN reached the result)
+    for b in B:
+        if torch.isnan(b["out"].float()).any():
+            raise RuntimeError("NaN in attention output")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, batches, args.cpu_sample_rows)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
+        "config": {"workload": desc, "name": args.workload, "batches_per_step": len(B),
+                   "query_tokens_per_step": tokens, "flops_per_step": flops},
+        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
+        "attn_only": {"ms_per_step": round(attn_total_ms, 4), "tflops": round(attn_tflops, 3),
+                      "mfma_peak_frac": round(attn_tflops / MFMA_PEAK_BF16, 4),
+                      "hbm_gbs_algorithmic": round(attn_gbs, 1), "per_launch_ms": [round(x, 4) for x in attn_ms]},
+        "roofline": roofline, "cpu_baseline": cpu, "setup_s": round(setup_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, batches, sample_rows):
+    """The CPU oracle, as it is, on a bounded sample of the same workload:
+    whole-prompt rows for the long-prompt case (the oracle's result for a row
+    does not depend on the chunking), sampled rows otherwise."""
+    import numpy as np
+
+    import oracle
+    from pkv_testlib import oracle_pools
+    import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    last = batches[-1]
+    if len(batches) > 1:                        # chunked prompt: the whole prompt as one full prefill
+        full = last.with_lengths([0], [int(last.kv_lens[0])])
+        pool_w = full
+    else:
+        full = last
+        pool_w = last
+    rows_total = int(full.chunk_lens.sum())
+    # at most 4 requests (spread over the batch), at most `sample_rows` rows among them
+    live = [b for b in range(full.batch) if int(full.chunk_lens[b]) > 0]
+    reqs = sorted(set(live[int(i)] for i in np.linspace(0, len(live) - 1, min(4, len(live)))))
+    sub = full.subset(reqs)
+    sub_qo, _ = oracle.extend_metadata(sub.prefix_lens, sub.chunk_lens)
+    n = min(int(sub.chunk_lens.sum()), sample_rows or 4097)
+    sub_rows = [int(r) for r in np.unique(np.linspace(0, int(sub.chunk_lens.sum()) - 1, n).astype(np.int64))]
+    # compact pool for the sampled requests
+    npg = [(int(n_) + sub.page_size - 1) // sub.page_size for n_ in sub.kv_lens]
+    pt = np.full((sub.batch, max(npg)), -1, np.int32)
+    off = 0
+    for b, c in enumerate(npg):
+        pt[b, :c] = np.arange(off, off + c)
+        off += c
+    import dataclasses
+    sub = dataclasses.replace(sub, page_table=pt, num_pages=off)
+    kp, vp = oracle_pools(sub)
+    q = wl.values(sub.q_all(), sub.dtype)
+    kf, vf = wl.values(kp, sub.dtype), wl.values(vp, sub.dtype)
+    t0 = time.perf_counter()
+    oracle.extend_attention(q, kf, vf, sub.page_table, sub.prefix_lens, sub.chunk_lens, window=sub.window,
+                            rows=sub_rows)
+    dt = time.perf_counter() - t0
+    flops = 0
+    for r in sub_rows:
+        b = int(np.searchsorted(sub_qo, r, side="right") - 1)
+        pos = int(sub.prefix_lens[b]) + r - int(sub_qo[b])
+        vis = pos + 1 if sub.window <= 0 else min(pos + 1, sub.window)
+        flops += 4 * sub.head_dim * sub.num_q_heads * vis
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3), "tokens_per_s": round(len(sub_rows) / dt, 2),
+            "sample": f"{len(sub_rows)} of {rows_total} query rows (all heads), fp32 NumPy oracle"}
+
+
+if __name__ == "__main__":
+    main()
