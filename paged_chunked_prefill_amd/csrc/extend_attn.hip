@@ -64,6 +64,7 @@ struct Params {
   int32_t num_kv_heads;
   int32_t group;
   int32_t page_size;
+  int32_t page_shift;  // log2(page_size) when a power of two, else -1
   int32_t num_pages;
   int32_t window;
   int32_t total_q;
@@ -117,27 +118,35 @@ __device__ inline bool key_visible(int j, int qpos, int kv_begin, int kv_end, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16: 64-key tiles, 32x32x16 MFMA
+// bf16: 64-key tiles, 32x32x16 MFMA, K/V gathered straight into LDS
 // ---------------------------------------------------------------------------
+
+// Sixteen zero bytes per lane: the source of every key slot that must read as
+// zeros (positions outside the item's key range, or a page id outside the pool).
+__device__ __attribute__((aligned(16))) const uint32_t g_zero_rows[64 * 4] = {};
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int BC = kTileKeysBf16;         // keys per tile
-  static constexpr int KPITCH = D * 2 + 16;        // LDS bytes per K row (16 B pad: b128 reads conflict-free)
-  static constexpr int VPITCH = D * 2 + 32;        // LDS bytes per V row (32 B pad: transposing reads)
-  static constexpr int KBYTES = BC * KPITCH;
-  static constexpr int STAGE = KBYTES + BC * VPITCH;
-  static constexpr int CHUNKS = D / 8;             // 16-byte chunks per key row
-  static constexpr int KEYS_PER_PASS = 256 / CHUNKS;
-  static constexpr int LOADS = BC / KEYS_PER_PASS; // 16-byte loads per thread per tensor
+  static constexpr int BC = kTileKeysBf16;       // keys per tile
+  static constexpr int ROWB = D * 2;             // LDS bytes per key row (no padding; XOR swizzle instead)
+  static constexpr int TILEB = BC * ROWB;        // one K (or V) tile
+  static constexpr int STAGE = 2 * TILEB;        // K then V
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;            // rows one wave-wide 1 KiB load covers
+  static constexpr int LOADS = BC / RPI / kWaves;// such loads per wave per tensor and tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
+  // K rows: chunk c of row r lives at chunk c ^ (r mod CH) -> the 32 rows of a
+  // b128 read spread over all banks. V rows: chunk c at c ^ 2(r mod CH/2),
+  // which keeps chunk pairs adjacent for the 8-byte transposing reads.
+  static __device__ int kswz(int r) { return r & (CH - 1); }
+  static __device__ int vswz(int r) { return 2 * (r & (CH / 2 - 1)); }
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
+__global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
   const ItemView it = load_item(p);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -177,47 +186,57 @@ __global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
   const int t0 = (it.kv_begin / T::BC) * T::BC;
   const int ntiles = it.kv_end > it.kv_begin ? (it.kv_end - t0 + T::BC - 1) / T::BC : 0;
   const int32_t* pt = p.page_table + int64_t(it.pt_row) * p.page_table_stride;
-  const uint16_t* kpool = static_cast<const uint16_t*>(p.k_pool);
-  const uint16_t* vpool = static_cast<const uint16_t*>(p.v_pool);
-  const int chunk = tid % T::CHUNKS, key_in_pass = tid / T::CHUNKS;
-  const int64_t row_elems = int64_t(p.num_kv_heads) * D;
+  const char* kpool = static_cast<const char*>(p.k_pool);
+  const char* vpool = static_cast<const char*>(p.v_pool);
+  const int64_t slot_bytes = int64_t(p.num_kv_heads) * D * 2;
+  const int64_t head_off = int64_t(it.kv_head) * D * 2;
+  const int ps = p.page_size, ps_shift = p.page_shift;
 
-  u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  auto load_tile = [&](int kv0) {
+  // Gather: wave w's load i fills LDS rows RPI*(i*4+w) .. +RPI-1 of a tile; lane l
+  // covers row RPI*(i*4+w) + l/CH at LDS chunk l%CH, i.e. source chunk (l%CH) ^ swz(row).
+  const int lrow = lane / T::CH, lchunk = lane % T::CH;
+  int pg[T::LOADS];  // page ids of this lane's rows for the next tile to gather
+  auto fetch_pages = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int j = kv0 + key_in_pass + i * T::KEYS_PER_PASS;
-      kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (j >= it.kv_begin && j < it.kv_end) {
-        const int col = j / p.page_size;
-        const int page = pt[col];
-        if (page >= 0 && page < p.num_pages) {
-          const int64_t off = (int64_t(page) * p.page_size + (j - col * p.page_size)) * row_elems +
-                              int64_t(it.kv_head) * D + 8 * chunk;
-          kreg[i] = *reinterpret_cast<const u32x4*>(kpool + off);
-          vreg[i] = *reinterpret_cast<const u32x4*>(vpool + off);
-        } else {
-          atomicOr(p.status, PKV_STATUS_BAD_PAGE);
-        }
-      }
+      const int j = kv0 + T::RPI * (i * kWaves + wave) + lrow;
+      const bool in = j >= it.kv_begin && j < it.kv_end;
+      const int col = ps_shift >= 0 ? (j >> ps_shift) : j / ps;
+      pg[i] = in ? pt[col] : -1;
     }
   };
-  auto store_tile = [&](int stage) {
+  auto gather = [&](int kv0, int stage) {
     char* kb = smem + stage * T::STAGE;
-    char* vb = kb + T::KBYTES;
+    char* vb = kb + T::TILEB;
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int kr = key_in_pass + i * T::KEYS_PER_PASS;
-      *reinterpret_cast<u32x4*>(kb + kr * T::KPITCH + chunk * 16) = kreg[i];
-      *reinterpret_cast<u32x4*>(vb + kr * T::VPITCH + chunk * 16) = vreg[i];
+      const int row = T::RPI * (i * kWaves + wave) + lrow;
+      const int j = kv0 + row;
+      const int page = pg[i];
+      const char* ksrc = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
+      const char* vsrc = ksrc;
+      if (page >= 0 && page < p.num_pages) {
+        const int slot = ps_shift >= 0 ? (j & (ps - 1)) : j - (j / ps) * ps;
+        const int64_t base = (int64_t(page) * ps + slot) * slot_bytes + head_off;
+        ksrc = kpool + base + 16 * (lchunk ^ T::kswz(row));
+        vsrc = vpool + base + 16 * (lchunk ^ T::vswz(row));
+      } else if (page >= p.num_pages || page < -1) {
+        atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+      }
+      const int rb = T::RPI * (i * kWaves + wave);  // first row of this wave-wide load
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ksrc,
+                                       (__attribute__((address_space(3))) void*)(kb + rb * T::ROWB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vsrc,
+                                       (__attribute__((address_space(3))) void*)(vb + rb * T::ROWB), 16, 0, 0);
     }
   };
 
   if (ntiles > 0) {
-    load_tile(t0);
-    store_tile(0);
+    fetch_pages(t0);
+    gather(t0, 0);
+    if (ntiles > 1) fetch_pages(t0 + T::BC);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's gathers have landed
   __syncthreads();
 
   // lane roles in the transposing V reads: group g4 of 16 lanes, element e, column quad q4
@@ -227,21 +246,26 @@ __global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
   for (int tile = 0; tile < ntiles; ++tile) {
     const int kv0 = t0 + tile * T::BC;
     const int stage = tile & 1;
-    if (tile + 1 < ntiles) load_tile(kv0 + T::BC);
+    if (tile + 1 < ntiles) {
+      gather(kv0 + T::BC, stage ^ 1);
+      if (tile + 2 < ntiles) fetch_pages(kv0 + 2 * T::BC);
+    }
 
     if (wave_live) {
       const char* kb = smem + stage * T::STAGE;
-      const char* vb = kb + T::KBYTES;
+      const char* vb = kb + T::TILEB;
 
       // S^T[key][row] for two 32-key blocks
       f32x16 s[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         s[kb2] = f32x16{};
-        const char* krow = kb + (32 * kb2 + l32) * T::KPITCH + 16 * half;
+        const int krow = 32 * kb2 + l32;
+        const char* kr = kb + krow * T::ROWB;
+        const int sw = T::kswz(krow);
 #pragma unroll
         for (int ks = 0; ks < T::KSTEPS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ks + half) ^ sw));
           s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
         }
       }
@@ -267,7 +291,6 @@ __global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
       mx = other_half_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_off = m_new == -INFINITY ? 0.f : m_new * c;
-      const float alpha = fast_exp2(m_run * c - m_off);
 
       // P = exp2(S*c - m) in bf16, laid out as the B operand of O^T += V^T P^T
       bf16x8 pb[2][2];
@@ -280,10 +303,15 @@ __global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
           lsum += pj;
           pb[kb2][j >> 3][j & 7] = (__bf16)pj;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      // rescale only when some row's max moved (wave-uniform branch)
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run * c - m_off);
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
+        for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
+      }
+      l_run += lsum;
+      m_run = m_new;
 
 #pragma unroll
       for (int db = 0; db < T::DBLK; ++db) {
@@ -291,14 +319,14 @@ __global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
         for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
           for (int m2 = 0; m2 < 2; ++m2) {
-            // lane 16g+4e+q reads 4 d-values of key row (32kb2+16m2+4(g/2)+e [+8]) at d = 32db+16(g%2)+4q;
+            // lane 16g+4e+q reads 4 d-values of key row 32kb2+16m2+4(g/2)+e (and +8) at d = 32db+16(g%2)+4q;
             // the transpose hands lane l the keys 32kb2+16m2+8r+4(l/32)+e at d = 32db + l%32
-            const int krow = 32 * kb2 + 16 * m2 + 4 * (g4 >> 1) + e4;
-            const char* vaddr = vb + krow * T::VPITCH + (32 * db + 16 * (g4 & 1) + 4 * q4) * 2;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vaddr));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vaddr + 8 * T::VPITCH));
+            const int vrow = 32 * kb2 + 16 * m2 + 4 * (g4 >> 1) + e4;
+            const int chunk = 4 * db + 2 * (g4 & 1) + (q4 >> 1);
+            const char* va = vb + vrow * T::ROWB + 16 * (chunk ^ T::vswz(vrow)) + 8 * (q4 & 1);
+            const char* vh = vb + (vrow + 8) * T::ROWB + 16 * (chunk ^ T::vswz(vrow + 8)) + 8 * (q4 & 1);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vh));
             const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
             const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a32), pb[kb2][m2], o[db], 0,
@@ -308,7 +336,7 @@ __global__ __launch_bounds__(256) void extend_attn_bf16(const Params p) {
       }
     }
 
-    if (tile + 1 < ntiles) store_tile(stage ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile gathered, next pages fetched
     __syncthreads();
   }
 
@@ -614,6 +642,7 @@ int launch_extend_attn(const AttnArgs& a, void* stream) {
   p.num_kv_heads = a.shape.num_kv_heads;
   p.group = a.shape.num_q_heads / a.shape.num_kv_heads;
   p.page_size = a.shape.page_size;
+  p.page_shift = (a.shape.page_size & (a.shape.page_size - 1)) ? -1 : __builtin_ctz(a.shape.page_size);
   p.num_pages = a.shape.num_pages;
   p.window = a.window;
   p.total_q = a.total_q;
