@@ -557,35 +557,50 @@ struct CombineParams {
   const float* ml_part;
   const int32_t* split_rows;
   void* out;
+  int32_t n_rows;       // split rows x query heads
   int32_t num_q_heads;
   int32_t max_splits;
   int32_t total_q;
 };
 
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wave per (split row, query head): lane k holds split k's (max, sum); the
+// output loop then issues every split's partial loads back to back.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
-  const int slot = blockIdx.x;
-  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (head >= p.num_q_heads) return;
+  if (wid >= p.n_rows) return;
+  const int slot = wid / p.num_q_heads, head = wid - slot * p.num_q_heads;
   const int token = p.split_rows[2 * slot];
   const int ns = min(p.split_rows[2 * slot + 1], p.max_splits);
   if (token < 0 || token >= p.total_q) return;
   const int64_t base = (int64_t(slot) * p.num_q_heads + head) * p.max_splits;
-  float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, p.ml_part[(base + k) * 2]);
+  const float mk = lane < ns ? p.ml_part[(base + lane) * 2] : -INFINITY;
+  const float lk = lane < ns ? p.ml_part[(base + lane) * 2 + 1] : 0.f;
+  const float M = wave_max(mk);
+  const float wk = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
+  float den = wave_sum(wk * lk);
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int x = 0; x < PER; ++x) acc[x] = 0.f;
-  float den = 0.f;
+  const float* op = p.o_part + base * D + lane;
+#pragma unroll 8
   for (int k = 0; k < ns; ++k) {
-    const float mk = p.ml_part[(base + k) * 2];
-    const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
-    den += w * p.ml_part[(base + k) * 2 + 1];
-    const float* op = p.o_part + (base + k) * D;
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k));  // split k's weight
 #pragma unroll
-    for (int x = 0; x < PER; ++x) acc[x] = fmaf(w, op[lane + 64 * x], acc[x]);
+    for (int x = 0; x < PER; ++x) acc[x] = fmaf(w, op[k * D + 64 * x], acc[x]);
   }
   if (!(den > 0.f)) den = INFINITY;  // no visible key: output 0
   const int64_t orow = (int64_t(token) * p.num_q_heads + head) * D;
@@ -613,10 +628,10 @@ void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
     cp.split_rows = a.split_rows;
     cp.out = a.out;
     cp.num_q_heads = a.shape.num_q_heads;
+    cp.n_rows = a.n_split_rows * a.shape.num_q_heads;
     cp.max_splits = a.max_splits;
     cp.total_q = a.total_q;
-    hipLaunchKernelGGL((combine_splits<D, BF16>), dim3(a.n_split_rows, (a.shape.num_q_heads + 3) / 4), dim3(256),
-                       0, st, cp);
+    hipLaunchKernelGGL((combine_splits<D, BF16>), dim3((cp.n_rows + 3) / 4), dim3(256), 0, st, cp);
   }
 }
 

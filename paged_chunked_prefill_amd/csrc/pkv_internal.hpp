@@ -20,6 +20,12 @@ constexpr int kTileKeysF32 = 32;
 // Every split of a one-token row covers whole 64-key blocks, so the tile
 // boundaries of both instantiations stay aligned to absolute positions.
 constexpr int kSplitGranule = 64;
+// Resident attention workgroups per compute unit (two 4-wave groups: 2 waves
+// per SIMD), and the cap on KV splits of one prefill tile.
+constexpr int kSlotsPerCU = 2;
+constexpr int kMaxPrefillSplits = 16;
+// Compute units of an MI355X; the planner sizes splits for this machine.
+constexpr int kNominalCUs = 256;
 
 // One unit of attention work = one workgroup: a tile of consecutive chunk
 // tokens of one request, all G query heads of one KV head, over the key

@@ -58,7 +58,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   if (decode_splits < 0 || decode_splits > PKV_MAX_SPLITS)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "decode_splits must be in 0..%d (got %d)", PKV_MAX_SPLITS,
                      decode_splits);
-  if (num_cus < 1) num_cus = 256;
+  if (num_cus < 1) num_cus = kNominalCUs;
 
   const int32_t hq = shape->num_q_heads, hkv = shape->num_kv_heads;
   const int32_t group = hq / hkv;
@@ -102,29 +102,45 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     }
   }
 
-  // ---- KV splits for one-token rows (explicit count, or sized to fill the GPU)
+  // ---- KV splits.
+  // One-token rows: the explicit count, or enough splits to give the GPU about
+  // two items per compute unit. Prefill tiles: when the launch has fewer items
+  // than resident workgroup slots, the longest tiles are cut into key ranges of
+  // roughly equal cost so every slot gets work; a tile's cost is its 64-key
+  // blocks times its live 32-row waves.
+  auto granules_of = [](const Tile& t) {
+    return std::max(1, ceil_div(t.kv_hi, kSplitGranule) - t.kv_lo / kSplitGranule);
+  };
+  auto waves_of = [group](const Tile& t) { return ceil_div(int64_t(t.q_count) * group, 32); };
   int32_t base_items = 0, n_one = 0;
+  int64_t total_cost = 0;
   for (const Tile& t : tiles) {
     base_items += hkv;
     n_one += t.one_token;
+    total_cost += int64_t(hkv) * granules_of(t) * waves_of(t);
   }
   int32_t auto_splits = 1;
   if (decode_splits == 0 && n_one > 0 && base_items > 0)
     auto_splits = std::min<int32_t>(PKV_MAX_SPLITS, std::max<int32_t>(1, ceil_div(2LL * num_cus, base_items)));
+  const int64_t slots = int64_t(num_cus) * kSlotsPerCU;
+  const int64_t unit = base_items < slots ? std::max<int64_t>(1, (total_cost + slots - 1) / slots) : 0;
 
   std::vector<WorkItem> items;
   std::vector<int32_t> split_rows;  // pairs (token, splits)
   int32_t n_split_rows = 0, max_splits = 1;
   for (const Tile& t : tiles) {
     const int32_t g0 = t.kv_lo / kSplitGranule;
-    const int32_t g1 = ceil_div(t.kv_hi, kSplitGranule);
-    const int32_t granules = std::max(1, g1 - g0);
+    const int32_t granules = granules_of(t);
     int32_t splits = 1;
     if (t.one_token) {
       if (decode_splits > 0)
         splits = std::min(decode_splits, granules);
       else
         splits = std::min(auto_splits, std::max(1, granules / 2));
+    } else if (unit > 0) {
+      const int64_t want = (int64_t(granules) * waves_of(t) + unit - 1) / unit;
+      splits = int32_t(std::min<int64_t>({want, kMaxPrefillSplits, std::max(1, granules / 2)}));
+      splits = std::max(splits, 1);
     }
     int32_t part_row = -1;
     if (splits > 1) {

@@ -48,8 +48,10 @@ def test_indptrs_bit_exact():
     assert np.array_equal(h["qo_indptr"], qo) and np.array_equal(h["kv_indptr"], kv)
     assert np.array_equal(h["prefix_lens"], w.prefix_lens)
     assert p.plan.total_q == 705 and p.plan.max_q_len == 512 and p.plan.max_kv_len == 1537
-    assert p.plan.n_items == 184            # (1 + 2 + 4 + 16) tiles x 8 KV heads
     assert h["status"][0] == 0
+    # (1 + 2 + 4 + 16) tiles x 8 KV heads = 184 < 512 resident slots: long tiles are split over KV
+    tiles = {(int(i["req"]), int(i["kv_head"]), int(i["q_begin"])) for i in h["items"]}
+    assert len(tiles) == 184 and p.plan.n_items > 184 and p.plan.n_split_rows > 0
 
 
 def coverage(p, P, L, hq, hkv, window):
@@ -115,12 +117,18 @@ def test_config5_split_plan():
 
 
 def test_window_ranges_are_tight():
+    """The key ranges of a tile's items (one item, or its splits) together span
+    exactly [first row's window start, last row's position + 1)."""
     P, L = np.array([6000], np.int32), np.array([1000], np.int32)
     p = pkv.build_extend_metadata(P, L, shape(32, 8, 128, 16, 1000), 4096, 0)
+    span = {}
     for it in p.host_sections()["items"]:
-        first = 6000 + int(it["q_begin"])
-        last = first + int(it["q_count"]) - 1
-        assert it["kv_begin"] == first - 4096 + 1 and it["kv_end"] == last + 1
+        key = (int(it["kv_head"]), int(it["q_begin"]), int(it["q_count"]))
+        lo, hi = span.get(key, (1 << 30, -1))
+        span[key] = (min(lo, int(it["kv_begin"])), max(hi, int(it["kv_end"])))
+    for (_, q0, n), (lo, hi) in span.items():
+        first = 6000 + q0
+        assert lo == first - 4096 + 1 and hi == first + n
 
 
 def status_of(fn):
@@ -194,3 +202,17 @@ def test_auto_splits_follow_the_cu_heuristic():
     # one-token rows with very short KV are not split below 2 blocks of 64 keys per split
     p = pkv.build_extend_metadata([100], [1], shape(32, 8, 128, 16, 8000), 0, 0)
     assert p.plan.max_splits == 1
+
+
+def test_prefill_tiles_split_only_when_few():
+    """A launch with fewer items than 2 per compute unit cuts its longest tiles
+    over KV (whole 64-key blocks, >= 2 per split); a full launch is not cut."""
+    s16 = shape(16, 4, 128, 64, 1000)
+    few = pkv.build_extend_metadata([3584], [512], s16)          # 16 tiles x 4 heads = 64 items
+    h = few.host_sections()
+    assert few.plan.n_items > 64 and few.plan.max_splits <= 16
+    for it in h["items"]:
+        if it["part_row"] >= 0:
+            assert it["kv_end"] - it["kv_begin"] >= 64
+    many = pkv.build_extend_metadata([16384, 16384], [2048, 2048], shape(64, 8, 128, 16, 5000))
+    assert many.plan.n_items == 2 * 8 * 128 and many.plan.n_split_rows == 0
