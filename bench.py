@@ -110,6 +110,8 @@ def main():
     from gpu_harness import DeviceCache, shape_of, to_dev, upload_q
 
     torch.cuda.set_device(0)
+    if args.workload == "copy_calibration":
+        return copy_calibration(args)
     if not pkv.device_supported(0):
         raise SystemExit("device 0 is not gfx950")
     lib = pkv.lib()
@@ -229,6 +231,20 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "setup_s": round(setup_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_calibration(args):
+    """A plain device copy of a known size (256 MiB read + 256 MiB written per
+    launch), to scale the FETCH_SIZE / WRITE_SIZE counters of the kernels."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy_calibration", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": args.warmup + args.steps}), flush=True)
 
 
 def cpu_baseline(w, batches, sample_rows):

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "pkv_internal.hpp"
 
@@ -125,6 +126,11 @@ __device__ inline bool key_visible(int j, int qpos, int kv_begin, int kv_end, in
 // zeros (positions outside the item's key range, or a page id outside the pool).
 __device__ __attribute__((aligned(16))) const uint32_t g_zero_rows[64 * 4] = {};
 
+// Scores are kept relative to a per-row reference max m_ref (log2 units); it is
+// only raised when a row's true max exceeds it by more than this, so P = 2^(s-m_ref)
+// stays below 2^kRescaleSlack and the O rescale is rare.
+constexpr float kRescaleSlack = 8.f;
+
 template <int D>
 struct Bf16Tile {
   static constexpr int BC = kTileKeysBf16;       // keys per tile
@@ -133,7 +139,8 @@ struct Bf16Tile {
   static constexpr int STAGE = 2 * TILEB;        // K then V
   static constexpr int CH = D / 8;               // 16-byte chunks per row
   static constexpr int RPI = 64 / CH;            // rows one wave-wide 1 KiB load covers
-  static constexpr int LOADS = BC / RPI / kWaves;// such loads per wave per tensor and tile
+  static constexpr int NW = kWavesBf16;          // waves per workgroup
+  static constexpr int LOADS = BC / RPI / NW;    // such loads per wave per tensor and tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   // K rows: chunk c of row r lives at chunk c ^ (r mod CH) -> the 32 rows of a
@@ -143,13 +150,18 @@ struct Bf16Tile {
   static __device__ int vswz(int r) { return 2 * (r & (CH / 2 - 1)); }
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
+template <int D, bool UNIFORM_PAGES>
+__global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+  // One array per stage: the compiler can then tell that a gather in flight into
+  // one stage never aliases the reads of the other, and does not make those
+  // reads wait for it.
+  __shared__ __attribute__((aligned(1024))) char smem0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[T::STAGE];
 
   const ItemView it = load_item(p);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int G = p.group;
 
@@ -180,106 +192,131 @@ __global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
   f32x16 o[T::DBLK];
 #pragma unroll
   for (int db = 0; db < T::DBLK; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of this row's raw scores
-  float l_run = 0.f;        // running sum of exp over the keys this lane holds
+  float m_ref = -INFINITY;  // reference max of this row, log2 units (scaled scores)
+  float l_run = 0.f;        // running sum of 2^(s - m_ref) over the keys this lane holds
 
   const int t0 = (it.kv_begin / T::BC) * T::BC;
   const int ntiles = it.kv_end > it.kv_begin ? (it.kv_end - t0 + T::BC - 1) / T::BC : 0;
   const int32_t* pt = p.page_table + int64_t(it.pt_row) * p.page_table_stride;
   const char* kpool = static_cast<const char*>(p.k_pool);
   const char* vpool = static_cast<const char*>(p.v_pool);
-  const int64_t slot_bytes = int64_t(p.num_kv_heads) * D * 2;
-  const int64_t head_off = int64_t(it.kv_head) * D * 2;
   const int ps = p.page_size, ps_shift = p.page_shift;
+  const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * 2;
+  const uint32_t page_bytes = uint32_t(ps) * row_bytes;  // < 2^31, checked on the host
+  const int kv_last = it.kv_end - 1;
 
-  // Gather: wave w's load i fills LDS rows RPI*(i*4+w) .. +RPI-1 of a tile; lane l
-  // covers row RPI*(i*4+w) + l/CH at LDS chunk l%CH, i.e. source chunk (l%CH) ^ swz(row).
-  const int lrow = lane / T::CH, lchunk = lane % T::CH;
-  int pg[T::LOADS];  // page ids of this lane's rows for the next tile to gather
+  // Gather: wave w's load i fills LDS rows RPI*(4i+w) .. +RPI-1 of a tile; lane l
+  // covers row RPI*(4i+w) + l/CH at LDS chunk l%CH, i.e. source chunk (l%CH) ^ swz(row).
+  // Both swizzles depend on the row only modulo CH, the same for every i. A key
+  // outside [kv_begin, kv_end) reads the nearest key inside the range instead:
+  // finite data that the mask turns into a -inf score and a zero weight, and no
+  // slot past the request's positions is ever touched. With UNIFORM_PAGES (the
+  // page size a multiple of RPI) the RPI rows of one load share a page, so the
+  // page id is one scalar load per load and the address is a scalar base plus a
+  // 32-bit lane offset.
+  const int lrow = lane / T::CH;
+  const int srow = T::RPI * wave + lrow;   // row modulo CH decides both swizzles
+  const uint32_t src_k = uint32_t(it.kv_head) * D * 2 + 16 * ((lane % T::CH) ^ T::kswz(srow));
+  const uint32_t src_v = uint32_t(it.kv_head) * D * 2 + 16 * ((lane % T::CH) ^ T::vswz(srow));
+  const char* zero = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
+  auto clampk = [&](int j) { return min(max(j, it.kv_begin), kv_last); };
+  auto page_col = [&](int j) { return ps_shift >= 0 ? (j >> ps_shift) : j / ps; };
+  int pg[T::LOADS];  // page ids for the next tile to gather
+  bool bad_page = false;
+  // Uniform page ids are read through the constant address space: scalar loads,
+  // which count on lgkmcnt and so never make the wave wait for gathers in flight.
+  const __attribute__((address_space(4))) int32_t* pt_const = (const __attribute__((address_space(4))) int32_t*)pt;
   auto fetch_pages = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int j = kv0 + T::RPI * (i * kWaves + wave) + lrow;
-      const bool in = j >= it.kv_begin && j < it.kv_end;
-      const int col = ps_shift >= 0 ? (j >> ps_shift) : j / ps;
-      pg[i] = in ? pt[col] : -1;
+      const int blk = kv0 + T::RPI * (T::NW * i + wave);
+      if (UNIFORM_PAGES)
+        pg[i] = pt_const[page_col(clampk(blk))];
+      else
+        pg[i] = pt[page_col(clampk(blk + lrow))];
     }
   };
-  auto gather = [&](int kv0, int stage) {
-    char* kb = smem + stage * T::STAGE;
-    char* vb = kb + T::TILEB;
+  auto gather = [&](int kv0, auto stage_c) {
+    char* kb = decltype(stage_c)::value ? smem1 : smem0;
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int row = T::RPI * (i * kWaves + wave) + lrow;
-      const int j = kv0 + row;
+      const int j = clampk(kv0 + T::RPI * (T::NW * i + wave) + lrow);
+      const int slot = ps_shift >= 0 ? (j & (ps - 1)) : j - (j / ps) * ps;
       const int page = pg[i];
-      const char* ksrc = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
-      const char* vsrc = ksrc;
-      if (page >= 0 && page < p.num_pages) {
-        const int slot = ps_shift >= 0 ? (j & (ps - 1)) : j - (j / ps) * ps;
-        const int64_t base = (int64_t(page) * ps + slot) * slot_bytes + head_off;
-        ksrc = kpool + base + 16 * (lchunk ^ T::kswz(row));
-        vsrc = vpool + base + 16 * (lchunk ^ T::vswz(row));
-      } else if (page >= p.num_pages || page < -1) {
-        atomicOr(p.status, PKV_STATUS_BAD_PAGE);
-      }
-      const int rb = T::RPI * (i * kWaves + wave);  // first row of this wave-wide load
+      const bool ok = page >= 0 && page < p.num_pages;
+      bad_page |= !ok;
+      const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes;
+      const uint32_t off = uint32_t(slot) * row_bytes;
+      const char* ksrc = ok ? kpool + pbase + (off + src_k) : zero;
+      const char* vsrc = ok ? vpool + pbase + (off + src_v) : zero;
+      char* dst = kb + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this wave-wide load
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ksrc,
-                                       (__attribute__((address_space(3))) void*)(kb + rb * T::ROWB), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vsrc,
-                                       (__attribute__((address_space(3))) void*)(vb + rb * T::ROWB), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(dst + T::TILEB), 16, 0, 0);
     }
   };
 
+  // per-lane LDS read offsets (stage base and the row-block terms are immediates)
+  // K (A operand of S^T): row l32 (+32 for the second key block), chunk (2ks+half) ^ swz
+  int koff[T::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < T::KSTEPS; ++ks) koff[ks] = l32 * T::ROWB + 16 * ((2 * ks + half) ^ T::kswz(l32));
+  // V (A operand of O^T += V^T P^T via transposing reads): lane 16g+4e+q reads row
+  // 4(g/2)+e (+ 32kb2 + 16m2 + 8hi) at d = 32db + 16(g%2) + 4q
+  int voff[T::DBLK];
+  {
+    const int g4 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+    const int vr = 4 * (g4 >> 1) + e4;
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db)
+      voff[db] = T::TILEB + vr * T::ROWB + 16 * ((4 * db + 2 * (g4 & 1) + (q4 >> 1)) ^ T::vswz(vr)) + 8 * (q4 & 1);
+  }
+
   if (ntiles > 0) {
     fetch_pages(t0);
-    gather(t0, 0);
+    gather(t0, std::integral_constant<int, 0>{});
     if (ntiles > 1) fetch_pages(t0 + T::BC);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's gathers have landed
   __syncthreads();
 
-  // lane roles in the transposing V reads: group g4 of 16 lanes, element e, column quad q4
-  const int g4 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
   const float c = p.scale_log2;
+  const int window = p.window;
 
-  for (int tile = 0; tile < ntiles; ++tile) {
+  auto process = [&](int tile, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     const int kv0 = t0 + tile * T::BC;
-    const int stage = tile & 1;
     if (tile + 1 < ntiles) {
-      gather(kv0 + T::BC, stage ^ 1);
+      gather(kv0 + T::BC, std::integral_constant<int, stage ^ 1>{});
       if (tile + 2 < ntiles) fetch_pages(kv0 + 2 * T::BC);
     }
-
     if (wave_live) {
-      const char* kb = smem + stage * T::STAGE;
-      const char* vb = kb + T::TILEB;
+      const char* kb = stage ? smem1 : smem0;
 
       // S^T[key][row] for two 32-key blocks
       f32x16 s[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         s[kb2] = f32x16{};
-        const int krow = 32 * kb2 + l32;
-        const char* kr = kb + krow * T::ROWB;
-        const int sw = T::kswz(krow);
 #pragma unroll
         for (int ks = 0; ks < T::KSTEPS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ks + half) ^ sw));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + koff[ks] + 32 * kb2 * T::ROWB);
           s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
         }
       }
 
       // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
       const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
-                        (p.window <= 0 || kv0 > qpos_last - p.window);
+                        (window <= 0 || kv0 > qpos_last - window);
       if (!full) {
+        const int kbase = kv0 + 4 * half;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int key = kv0 + 32 * kb2 + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (!key_visible(key, qpos, it.kv_begin, it.kv_end, p.window)) s[kb2][j] = -INFINITY;
+            const int key = kbase + 32 * kb2 + 8 * (j >> 2) + (j & 3);
+            if (!key_visible(key, qpos, it.kv_begin, it.kv_end, window)) s[kb2][j] = -INFINITY;
           }
       }
 
@@ -288,11 +325,21 @@ __global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
-      mx = other_half_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_off = m_new == -INFINITY ? 0.f : m_new * c;
+      mx = other_half_max(mx) * c;   // this row's max over the tile, log2 units
+      // raise the reference only when the true max outruns it by more than the slack
+      const bool raise = mx > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float m_new = raise ? mx : m_ref;
+        // lanes that keep their reference (possibly still -inf) must not compute -inf - -inf
+        const float alpha = raise ? fast_exp2(m_ref - m_new) : 1.f;   // 0 when m_ref was -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_off = m_ref == -INFINITY ? 0.f : m_ref;
 
-      // P = exp2(S*c - m) in bf16, laid out as the B operand of O^T += V^T P^T
+      // P = exp2(S*c - m_ref) in bf16, laid out as the B operand of O^T += V^T P^T
       bf16x8 pb[2][2];
       float lsum = 0.f;
 #pragma unroll
@@ -303,15 +350,7 @@ __global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
           lsum += pj;
           pb[kb2][j >> 3][j & 7] = (__bf16)pj;
         }
-      // rescale only when some row's max moved (wave-uniform branch)
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
-        const float alpha = fast_exp2(m_run * c - m_off);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
-      }
       l_run += lsum;
-      m_run = m_new;
 
 #pragma unroll
       for (int db = 0; db < T::DBLK; ++db) {
@@ -319,14 +358,11 @@ __global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
         for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
           for (int m2 = 0; m2 < 2; ++m2) {
-            // lane 16g+4e+q reads 4 d-values of key row 32kb2+16m2+4(g/2)+e (and +8) at d = 32db+16(g%2)+4q;
             // the transpose hands lane l the keys 32kb2+16m2+8r+4(l/32)+e at d = 32db + l%32
-            const int vrow = 32 * kb2 + 16 * m2 + 4 * (g4 >> 1) + e4;
-            const int chunk = 4 * db + 2 * (g4 & 1) + (q4 >> 1);
-            const char* va = vb + vrow * T::ROWB + 16 * (chunk ^ T::vswz(vrow)) + 8 * (q4 & 1);
-            const char* vh = vb + (vrow + 8) * T::ROWB + 16 * (chunk ^ T::vswz(vrow + 8)) + 8 * (q4 & 1);
+            const char* va = kb + voff[db] + (32 * kb2 + 16 * m2) * T::ROWB;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vh));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va + 8 * T::ROWB));
             const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
             const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a32), pb[kb2][m2], o[db], 0,
@@ -335,10 +371,15 @@ __global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
         }
       }
     }
-
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile gathered, next pages fetched
     __syncthreads();
+  };
+
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    process(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 < ntiles) process(tile + 1, std::integral_constant<int, 1>{});
   }
+  if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
 
   if (!wave_live) return;
   const float l_tot = other_half_sum(l_run);
@@ -369,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void extend_attn_bf16(const Params p) {
         *reinterpret_cast<f32x4*>(op + 32 * db + 8 * jj + 4 * half) = v;
       }
     if (half == 0) {
-      p.ml_part[prow * 2] = m_run == -INFINITY ? -INFINITY : m_run * c;
+      p.ml_part[prow * 2] = m_ref;   // reference max (log2 units) the partial is relative to
       p.ml_part[prow * 2 + 1] = l_tot;
     }
   }
@@ -616,8 +657,13 @@ __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
 template <int D, bool BF16>
 void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
   if (a.n_items > 0) {
-    if (BF16)
-      hipLaunchKernelGGL(extend_attn_bf16<D>, dim3(a.n_items), dim3(256), 0, st, p);
+    if (BF16) {
+      // the rows of one wave-wide gather share a page when the page size is a multiple of them
+      if (a.shape.page_size % Bf16Tile<D>::RPI == 0)
+        hipLaunchKernelGGL((extend_attn_bf16<D, true>), dim3(a.n_items), dim3(64 * kWavesBf16), 0, st, p);
+      else
+        hipLaunchKernelGGL((extend_attn_bf16<D, false>), dim3(a.n_items), dim3(64 * kWavesBf16), 0, st, p);
+    }
     else
       hipLaunchKernelGGL(extend_attn_f32<D>, dim3(a.n_items), dim3(256), 0, st, p);
   }

@@ -9,23 +9,30 @@
 
 namespace pkv {
 
-// Query-head rows per attention workgroup: four waves of 32 rows each. Rows
-// are (token, head-in-group) pairs of one KV head, token-major, so a tile
-// holds ROWS / G consecutive chunk tokens.
-constexpr int kWaves = 4;
-constexpr int kRows = 32 * kWaves;
+// Query-head rows per attention work item: waves of 32 rows each. Rows are
+// (token, head-in-group) pairs of one KV head, token-major, so a tile holds
+// rows / G consecutive chunk tokens. The bf16 kernel runs 8 waves (256 rows)
+// per workgroup, one workgroup per CU (2 waves per SIMD): every K/V tile staged
+// in LDS then serves 256 rows. The fp32 kernel runs 4 waves (128 rows), two
+// workgroups per CU.
+constexpr int kWavesBf16 = 8;
+constexpr int kWavesF32 = 4;
+constexpr int kMaxGroup = 128;  // largest GQA group size (query heads per KV head)
+inline int waves_per_item(int dtype) { return dtype == PKV_DTYPE_BF16 ? kWavesBf16 : kWavesF32; }
+inline int rows_per_item(int dtype) { return 32 * waves_per_item(dtype); }
+inline int slots_per_cu(int dtype) { return dtype == PKV_DTYPE_BF16 ? 1 : 2; }
 // Keys per KV tile staged in LDS (bf16 / fp32 instantiations).
 constexpr int kTileKeysBf16 = 64;
 constexpr int kTileKeysF32 = 32;
 // Every split of a one-token row covers whole 64-key blocks, so the tile
 // boundaries of both instantiations stay aligned to absolute positions.
 constexpr int kSplitGranule = 64;
-// Resident attention workgroups per compute unit (two 4-wave groups: 2 waves
-// per SIMD), and the cap on KV splits of one prefill tile.
-constexpr int kSlotsPerCU = 2;
+// Cap on the KV splits of one prefill tile.
 constexpr int kMaxPrefillSplits = 16;
 // Compute units of an MI355X; the planner sizes splits for this machine.
 constexpr int kNominalCUs = 256;
+// XCDs (each with its own L2); workgroups are dispatched to them round-robin.
+constexpr int kXcds = 8;
 
 // One unit of attention work = one workgroup: a tile of consecutive chunk
 // tokens of one request, all G query heads of one KV head, over the key

@@ -13,6 +13,7 @@
 // ranges (causal and window bounds), and split slots for the combine step.
 #include <algorithm>
 #include <cstring>
+#include <tuple>
 #include <vector>
 
 #include "pkv_internal.hpp"
@@ -33,8 +34,12 @@ int validate_shape(const pkv_shape* s) {
     return set_error(PKV_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = fp32)", s->dtype);
   if (s->head_dim != 64 && s->head_dim != 128)
     return set_error(PKV_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", s->head_dim);
-  if (s->num_q_heads / s->num_kv_heads > kRows)
-    return set_error(PKV_ERR_UNSUPPORTED, "GQA group size %d exceeds %d", s->num_q_heads / s->num_kv_heads, kRows);
+  const int64_t page_bytes = int64_t(s->page_size) * s->num_kv_heads * s->head_dim * (s->dtype == PKV_DTYPE_BF16 ? 2 : 4);
+  if (page_bytes > INT32_MAX)
+    return set_error(PKV_ERR_UNSUPPORTED, "one page of one pool spans %lld bytes (at most 2^31-1 supported)",
+                     (long long)page_bytes);
+  if (s->num_q_heads / s->num_kv_heads > kMaxGroup)
+    return set_error(PKV_ERR_UNSUPPORTED, "GQA group size %d exceeds %d", s->num_q_heads / s->num_kv_heads, kMaxGroup);
   return PKV_OK;
 }
 
@@ -46,6 +51,61 @@ struct Tile {
 };
 
 int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
+
+// Reorder items so that position i (dispatched to XCD i % kXcds) holds work of
+// the locality group assigned to that XCD; see the dispatch-order comment in
+// plan_extend. Falls back to plain longest-first when there are fewer items
+// than XCDs.
+template <class Cost>
+std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
+  std::vector<WorkItem> items = in;
+  std::stable_sort(items.begin(), items.end(),
+                   [&](const WorkItem& a, const WorkItem& b) { return cost(a) > cost(b); });
+  const size_t n = items.size();
+  if (n < size_t(kXcds) * 2) return items;
+  // locality groups: items with equal (request, KV head, split)
+  auto key = [](const WorkItem& a) { return std::make_tuple(a.req, a.kv_head, a.split); };
+  std::vector<uint32_t> by_key(n);
+  for (size_t i = 0; i < n; ++i) by_key[i] = uint32_t(i);
+  std::stable_sort(by_key.begin(), by_key.end(),
+                   [&](uint32_t a, uint32_t b) { return key(items[a]) < key(items[b]); });
+  std::vector<uint32_t> group_of(n);
+  std::vector<int64_t> group_cost;
+  for (size_t k = 0; k < n; ++k) {
+    if (k == 0 || key(items[by_key[k]]) != key(items[by_key[k - 1]])) group_cost.push_back(0);
+    group_of[by_key[k]] = uint32_t(group_cost.size() - 1);
+    group_cost.back() += cost(items[by_key[k]]);
+  }
+  std::vector<uint32_t> groups(group_cost.size());
+  for (size_t g = 0; g < groups.size(); ++g) groups[g] = uint32_t(g);
+  std::stable_sort(groups.begin(), groups.end(), [&](uint32_t a, uint32_t b) { return group_cost[a] > group_cost[b]; });
+  int64_t load[kXcds] = {};
+  std::vector<uint8_t> xcd_of(group_cost.size());
+  for (uint32_t g : groups) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += group_cost[g];
+    xcd_of[g] = uint8_t(best);
+  }
+  std::vector<std::vector<uint32_t>> per(kXcds);
+  for (size_t i = 0; i < n; ++i) per[xcd_of[group_of[i]]].push_back(uint32_t(i));  // keeps cost order
+  std::vector<WorkItem> out;
+  out.reserve(n);
+  size_t next[kXcds] = {};
+  for (size_t i = 0; out.size() < n; ++i) {
+    int x = int(i % kXcds);
+    if (next[x] >= per[x].size()) {
+      // this XCD's list is used up: hand its slot the next item of the fullest list
+      int best = -1;
+      for (int y = 0; y < kXcds; ++y)
+        if (next[y] < per[y].size() && (best < 0 || per[y].size() - next[y] > per[best].size() - next[best])) best = y;
+      x = best;
+    }
+    out.push_back(items[per[x][next[x]++]]);
+  }
+  return out;
+}
 
 }  // namespace
 
@@ -62,7 +122,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
 
   const int32_t hq = shape->num_q_heads, hkv = shape->num_kv_heads;
   const int32_t group = hq / hkv;
-  const int32_t tile_tokens = std::max(1, kRows / group);
+  const int32_t tile_tokens = std::max(1, rows_per_item(shape->dtype) / group);
 
   // ---- per-request sums (int32 range checked in 64-bit)
   int64_t total_q = 0, total_kv = 0;
@@ -122,7 +182,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   int32_t auto_splits = 1;
   if (decode_splits == 0 && n_one > 0 && base_items > 0)
     auto_splits = std::min<int32_t>(PKV_MAX_SPLITS, std::max<int32_t>(1, ceil_div(2LL * num_cus, base_items)));
-  const int64_t slots = int64_t(num_cus) * kSlotsPerCU;
+  const int64_t slots = int64_t(num_cus) * slots_per_cu(shape->dtype);
   const int64_t unit = base_items < slots ? std::max<int64_t>(1, (total_cost + slots - 1) / slots) : 0;
 
   std::vector<WorkItem> items;
@@ -178,14 +238,17 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     }
   }
 
-  // Longest work first, so the long items start early and short ones fill the
-  // tail. An item's time grows with its key range times its live 32-row waves.
+  // Dispatch order. Workgroups go to the 8 XCDs round-robin (workgroup i runs on
+  // XCD i mod 8), and each XCD has its own L2. Items that read the same keys --
+  // same request, KV head and split -- are grouped and each group is placed on
+  // one XCD (groups assigned greedily to the least-loaded XCD, largest first),
+  // so the tiles that stream one KV head stay together in one L2. Within an XCD
+  // the longest items go first; an item's time grows with its key range times
+  // its live 32-row waves.
   auto cost = [group](const WorkItem& a) {
     return int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
   };
-  std::stable_sort(items.begin(), items.end(),
-                   [&](const WorkItem& a, const WorkItem& b) { return cost(a) > cost(b); });
-
+  items = xcd_order(items, cost);
   const int32_t n_items = int32_t(items.size());
   const MetaLayout lay = meta_layout(batch, n_items, n_split_rows);
   if (meta_bytes_out) *meta_bytes_out = lay.total;

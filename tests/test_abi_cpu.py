@@ -49,9 +49,10 @@ def test_indptrs_bit_exact():
     assert np.array_equal(h["prefix_lens"], w.prefix_lens)
     assert p.plan.total_q == 705 and p.plan.max_q_len == 512 and p.plan.max_kv_len == 1537
     assert h["status"][0] == 0
-    # (1 + 2 + 4 + 16) tiles x 8 KV heads = 184 < 512 resident slots: long tiles are split over KV
+    # bf16 items hold 256 query-head rows = 64 tokens x 4 heads: (1 + 1 + 2 + 8) tiles x 8 KV heads
+    # = 96 < 256 resident slots, so the long tiles are split over KV
     tiles = {(int(i["req"]), int(i["kv_head"]), int(i["q_begin"])) for i in h["items"]}
-    assert len(tiles) == 184 and p.plan.n_items > 184 and p.plan.n_split_rows > 0
+    assert len(tiles) == 96 and p.plan.n_items > 96 and p.plan.n_split_rows > 0
 
 
 def coverage(p, P, L, hq, hkv, window):
@@ -109,7 +110,7 @@ def test_work_list_covers_every_row_once(cfg):
 def test_config5_split_plan():
     w = wl.config5()
     p = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape(64, 8, 128, 16, w.num_pages), 0, 8)
-    assert p.plan.n_items == 64 * 8 * 8 + 2 * 8 * (2048 // 16)
+    assert p.plan.n_items == 64 * 8 * 8 + 2 * 8 * (2048 // 32)      # 8 splits; 32-token tiles (G=8)
     assert p.plan.n_split_rows == 64 and p.plan.max_splits == 8
     assert p.plan.workspace_bytes >= 64 * 64 * 8 * (128 + 2) * 4
     mb, wb = pkv.extend_metadata_size(w.prefix_lens, w.chunk_lens, shape(64, 8, 128, 16, w.num_pages), 0, 8)
@@ -208,11 +209,11 @@ def test_prefill_tiles_split_only_when_few():
     """A launch with fewer items than 2 per compute unit cuts its longest tiles
     over KV (whole 64-key blocks, >= 2 per split); a full launch is not cut."""
     s16 = shape(16, 4, 128, 64, 1000)
-    few = pkv.build_extend_metadata([3584], [512], s16)          # 16 tiles x 4 heads = 64 items
+    few = pkv.build_extend_metadata([3584], [512], s16)          # 8 tiles x 4 heads = 32 items
     h = few.host_sections()
-    assert few.plan.n_items > 64 and few.plan.max_splits <= 16
+    assert few.plan.n_items > 32 and few.plan.max_splits <= 16
     for it in h["items"]:
         if it["part_row"] >= 0:
             assert it["kv_end"] - it["kv_begin"] >= 64
     many = pkv.build_extend_metadata([16384, 16384], [2048, 2048], shape(64, 8, 128, 16, 5000))
-    assert many.plan.n_items == 2 * 8 * 128 and many.plan.n_split_rows == 0
+    assert many.plan.n_items == 2 * 8 * 64 and many.plan.n_split_rows == 0
