@@ -123,7 +123,7 @@ __device__ inline bool key_visible(int j, int qpos, int kv_begin, int kv_end, in
 // ---------------------------------------------------------------------------
 
 // Sixteen zero bytes per lane: the source of every key slot that must read as
-// zeros (positions outside the item's key range, or a page id outside the pool).
+// zeros (a page id outside the pool).
 __device__ __attribute__((aligned(16))) const uint32_t g_zero_rows[64 * 4] = {};
 
 // Scores are kept relative to a per-row reference max m_ref (log2 units); it is
@@ -131,16 +131,43 @@ __device__ __attribute__((aligned(16))) const uint32_t g_zero_rows[64 * 4] = {};
 // stays below 2^kRescaleSlack and the O rescale is rare.
 constexpr float kRescaleSlack = 8.f;
 
+// s_waitcnt immediate: vmcnt(N), lgkmcnt(0), expcnt unchanged (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4);
+
+// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at LDS address `lds` + 16 l. Issued as inline asm so that the
+// compiler does not track these LDS writes (it would otherwise make every LDS
+// read wait for them); the kernel orders them itself with s_waitcnt vmcnt and
+// barriers. m0 is reserved by the compiler and set here for each copy.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy16(const void* vaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(vaddr), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int D>
 struct Bf16Tile {
   static constexpr int BC = kTileKeysBf16;       // keys per tile
   static constexpr int ROWB = D * 2;             // LDS bytes per key row (no padding; XOR swizzle instead)
   static constexpr int TILEB = BC * ROWB;        // one K (or V) tile
   static constexpr int STAGE = 2 * TILEB;        // K then V
+  static constexpr int NSTAGE = 4;               // LDS ring of tiles
   static constexpr int CH = D / 8;               // 16-byte chunks per row
-  static constexpr int RPI = 64 / CH;            // rows one wave-wide 1 KiB load covers
+  static constexpr int RPI = 64 / CH;            // rows one wave-wide 1 KiB copy covers
   static constexpr int NW = kWavesBf16;          // waves per workgroup
-  static constexpr int LOADS = BC / RPI / NW;    // such loads per wave per tensor and tile
+  static constexpr int LOADS = BC / RPI / NW;    // such copies per wave per tensor and tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   // K rows: chunk c of row r lives at chunk c ^ (r mod CH) -> the 32 rows of a
@@ -153,11 +180,8 @@ struct Bf16Tile {
 template <int D, bool UNIFORM_PAGES>
 __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
-  // One array per stage: the compiler can then tell that a gather in flight into
-  // one stage never aliases the reads of the other, and does not make those
-  // reads wait for it.
-  __shared__ __attribute__((aligned(1024))) char smem0[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
+  const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char*)smem));
 
   const ItemView it = load_item(p);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -205,28 +229,25 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   const uint32_t page_bytes = uint32_t(ps) * row_bytes;  // < 2^31, checked on the host
   const int kv_last = it.kv_end - 1;
 
-  // Gather: wave w's load i fills LDS rows RPI*(4i+w) .. +RPI-1 of a tile; lane l
-  // covers row RPI*(4i+w) + l/CH at LDS chunk l%CH, i.e. source chunk (l%CH) ^ swz(row).
+  // Gather: wave w's copy i fills LDS rows RPI*(NW*i+w) .. +RPI-1 of a tile; lane l
+  // covers row RPI*(NW*i+w) + l/CH at LDS chunk l%CH, i.e. source chunk (l%CH) ^ swz(row).
   // Both swizzles depend on the row only modulo CH, the same for every i. A key
   // outside [kv_begin, kv_end) reads the nearest key inside the range instead:
   // finite data that the mask turns into a -inf score and a zero weight, and no
   // slot past the request's positions is ever touched. With UNIFORM_PAGES (the
-  // page size a multiple of RPI) the RPI rows of one load share a page, so the
-  // page id is one scalar load per load and the address is a scalar base plus a
-  // 32-bit lane offset.
+  // page size a multiple of RPI) the RPI rows of one copy share a page: its id
+  // is one scalar load (constant address space, so it never waits on copies in
+  // flight) and the source is a scalar base plus a 32-bit lane offset.
   const int lrow = lane / T::CH;
   const int srow = T::RPI * wave + lrow;   // row modulo CH decides both swizzles
   const uint32_t src_k = uint32_t(it.kv_head) * D * 2 + 16 * ((lane % T::CH) ^ T::kswz(srow));
   const uint32_t src_v = uint32_t(it.kv_head) * D * 2 + 16 * ((lane % T::CH) ^ T::vswz(srow));
-  const char* zero = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
-  auto clampk = [&](int j) { return min(max(j, it.kv_begin), kv_last); };
-  auto page_col = [&](int j) { return ps_shift >= 0 ? (j >> ps_shift) : j / ps; };
+  auto clampk = [&](int j) __attribute__((always_inline)) { return min(max(j, it.kv_begin), kv_last); };
+  auto page_col = [&](int j) __attribute__((always_inline)) { return ps_shift >= 0 ? (j >> ps_shift) : j / ps; };
+  const __attribute__((address_space(4))) int32_t* pt_const = (const __attribute__((address_space(4))) int32_t*)pt;
   int pg[T::LOADS];  // page ids for the next tile to gather
   bool bad_page = false;
-  // Uniform page ids are read through the constant address space: scalar loads,
-  // which count on lgkmcnt and so never make the wave wait for gathers in flight.
-  const __attribute__((address_space(4))) int32_t* pt_const = (const __attribute__((address_space(4))) int32_t*)pt;
-  auto fetch_pages = [&](int kv0) {
+  auto fetch_pages = [&](int kv0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int blk = kv0 + T::RPI * (T::NW * i + wave);
@@ -236,8 +257,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
         pg[i] = pt[page_col(clampk(blk + lrow))];
     }
   };
-  auto gather = [&](int kv0, auto stage_c) {
-    char* kb = decltype(stage_c)::value ? smem1 : smem0;
+  auto gather = [&](int kv0, uint32_t stage_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int j = clampk(kv0 + T::RPI * (T::NW * i + wave) + lrow);
@@ -245,26 +265,31 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       const int page = pg[i];
       const bool ok = page >= 0 && page < p.num_pages;
       bad_page |= !ok;
-      const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes;
+      const uint32_t dst = stage_lds + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this copy
       const uint32_t off = uint32_t(slot) * row_bytes;
-      const char* ksrc = ok ? kpool + pbase + (off + src_k) : zero;
-      const char* vsrc = ok ? vpool + pbase + (off + src_v) : zero;
-      char* dst = kb + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this wave-wide load
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ksrc,
-                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vsrc,
-                                       (__attribute__((address_space(3))) void*)(dst + T::TILEB), 16, 0, 0);
+      if (UNIFORM_PAGES) {
+        const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes;
+        const char* kb = ok ? kpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
+        const char* vb = ok ? vpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
+        lds_copy16(kb, ok ? off + src_k : 16u * lane, dst);
+        lds_copy16(vb, ok ? off + src_v : 16u * lane, dst + T::TILEB);
+      } else {
+        const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes + off;
+        const char* zero = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
+        lds_copy16(ok ? kpool + pbase + src_k : zero, dst);
+        lds_copy16(ok ? vpool + pbase + src_v : zero, dst + T::TILEB);
+      }
     }
   };
 
-  // per-lane LDS read offsets (stage base and the row-block terms are immediates)
+  // per-lane LDS read offsets within a stage (the row-block terms are immediates)
   // K (A operand of S^T): row l32 (+32 for the second key block), chunk (2ks+half) ^ swz
-  int koff[T::KSTEPS];
+  uint32_t koff[T::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < T::KSTEPS; ++ks) koff[ks] = l32 * T::ROWB + 16 * ((2 * ks + half) ^ T::kswz(l32));
   // V (A operand of O^T += V^T P^T via transposing reads): lane 16g+4e+q reads row
   // 4(g/2)+e (+ 32kb2 + 16m2 + 8hi) at d = 32db + 16(g%2) + 4q
-  int voff[T::DBLK];
+  uint32_t voff[T::DBLK];
   {
     const int g4 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
     const int vr = 4 * (g4 >> 1) + e4;
@@ -273,111 +298,161 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       voff[db] = T::TILEB + vr * T::ROWB + 16 * ((4 * db + 2 * (g4 & 1) + (q4 >> 1)) ^ T::vswz(vr)) + 8 * (q4 & 1);
   }
 
-  if (ntiles > 0) {
-    fetch_pages(t0);
-    gather(t0, std::integral_constant<int, 0>{});
-    if (ntiles > 1) fetch_pages(t0 + T::BC);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's gathers have landed
-  __syncthreads();
-
+  // ---- ping-pong schedule -------------------------------------------------
+  // Waves w and w+4 share a SIMD. Group 0 (waves 0-3) and group 1 (waves 4-7)
+  // run the same per-tile program one segment apart, so that while one group
+  // issues its MFMA segment the other runs its softmax (VALU) segment:
+  //   segment S0: S(0) = K(0) Q^T                                     (prologue)
+  //   segment V:  mask, row max, rescale, P(t) = exp2(S(t) - m)       (VALU)
+  //   segment M:  O += V(t)^T P(t), then S(t+1) = K(t+1) Q^T           (MFMA)
+  // Slot j lies between block barriers j-1 and j; group 0 runs its segment j in
+  // slot j, group 1 in slot j+1. Tile u sits in LDS stage u % 4; its gather is
+  // issued in slot 2u-4 (once both groups have read tile u-4 from that stage)
+  // and must land before slot 2u, where group 0 first reads K(u). Every barrier
+  // first waits for this wave's gathers older than the newest one, so a gather
+  // has about three slots to land.
+  const int grp = wave >> 2;
   const float c = p.scale_log2;
   const int window = p.window;
+  bool newest_issued = false;   // was the most recent gather slot a real tile?
 
-  auto process = [&](int tile, auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
-    const int kv0 = t0 + tile * T::BC;
-    if (tile + 1 < ntiles) {
-      gather(kv0 + T::BC, std::integral_constant<int, stage ^ 1>{});
-      if (tile + 2 < ntiles) fetch_pages(kv0 + 2 * T::BC);
+  auto gather_tile = [&](int u) __attribute__((always_inline)) {
+    newest_issued = u < ntiles;
+    if (u < ntiles) {
+      gather(t0 + u * T::BC, lds0 + uint32_t(u & (T::NSTAGE - 1)) * T::STAGE);
+      if (u + 1 < ntiles) fetch_pages(t0 + (u + 1) * T::BC);
     }
-    if (wave_live) {
-      const char* kb = stage ? smem1 : smem0;
-
-      // S^T[key][row] for two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        s[kb2] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < T::KSTEPS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + koff[ks] + 32 * kb2 * T::ROWB);
-          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
-        }
-      }
-
-      // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
-      const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
-                        (window <= 0 || kv0 > qpos_last - window);
-      if (!full) {
-        const int kbase = kv0 + 4 * half;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = kbase + 32 * kb2 + 8 * (j >> 2) + (j & 3);
-            if (!key_visible(key, qpos, it.kv_begin, it.kv_end, window)) s[kb2][j] = -INFINITY;
-          }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
-      mx = other_half_max(mx) * c;   // this row's max over the tile, log2 units
-      // raise the reference only when the true max outruns it by more than the slack
-      const bool raise = mx > m_ref + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float m_new = raise ? mx : m_ref;
-        // lanes that keep their reference (possibly still -inf) must not compute -inf - -inf
-        const float alpha = raise ? fast_exp2(m_ref - m_new) : 1.f;   // 0 when m_ref was -inf
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_off = m_ref == -INFINITY ? 0.f : m_ref;
-
-      // P = exp2(S*c - m_ref) in bf16, laid out as the B operand of O^T += V^T P^T
-      bf16x8 pb[2][2];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float pj = fast_exp2(fmaf(s[kb2][j], c, -m_off));
-          lsum += pj;
-          pb[kb2][j >> 3][j & 7] = (__bf16)pj;
-        }
-      l_run += lsum;
-
-#pragma unroll
-      for (int db = 0; db < T::DBLK; ++db) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2) {
-            // the transpose hands lane l the keys 32kb2+16m2+8r+4(l/32)+e at d = 32db + l%32
-            const char* va = kb + voff[db] + (32 * kb2 + 16 * m2) * T::ROWB;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va + 8 * T::ROWB));
-            const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
-            const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a32), pb[kb2][m2], o[db], 0,
-                                                            0, 0);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile gathered, next pages fetched
-    __syncthreads();
+  };
+  // wait for LDS reads and for every gather but the newest, then the block barrier
+  auto sync = [&]() __attribute__((always_inline)) {
+    if (UNIFORM_PAGES && newest_issued)
+      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * T::LOADS>);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    process(tile, std::integral_constant<int, 0>{});
-    if (tile + 1 < ntiles) process(tile + 1, std::integral_constant<int, 1>{});
+  f32x16 s[2];            // scores S^T of the tile in flight (two 32-key blocks)
+  bf16x8 pb[2][2];        // P of the tile being accumulated, as B operands
+  auto seg_S = [&](int u) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    const char* kb = smem + (u & (T::NSTAGE - 1)) * T::STAGE;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < T::KSTEPS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + koff[ks] + 32 * kb2 * T::ROWB);
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
+      }
+    }
+  };
+  auto seg_V = [&](int t) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    const int kv0 = t0 + t * T::BC;
+    // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
+    const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
+                      (window <= 0 || kv0 > qpos_last - window);
+    if (!full) {
+      // this row sees keys lo..hi of the item's range (one unsigned test per key)
+      int lo = it.kv_begin, hi = min(kv_last, qpos);
+      if (window > 0) lo = max(lo, qpos - window + 1);
+      if (hi < lo) lo = hi = kv0 + T::BC;   // nothing visible in this tile
+      const uint32_t width = uint32_t(hi - lo);
+      const int d0 = kv0 + 4 * half - lo;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (uint32_t(d0 + 32 * kb2 + 8 * (j >> 2) + (j & 3)) > width) s[kb2][j] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
+    mx = other_half_max(mx) * c;   // this row's max over the tile, log2 units
+    // raise the reference only when the true max outruns it by more than the slack
+    const bool raise = mx > m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mx : m_ref;
+      // lanes that keep their reference (possibly still -inf) must not compute -inf - -inf
+      const float alpha = raise ? fast_exp2(m_ref - m_new) : 1.f;   // 0 when m_ref was -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_off = m_ref == -INFINITY ? 0.f : m_ref;
+    // P = exp2(S*c - m_ref) in bf16, laid out as the B operand of O^T += V^T P^T
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pj = fast_exp2(fmaf(s[kb2][j], c, -m_off));
+        lsum += pj;
+        pb[kb2][j >> 3][j & 7] = (__bf16)pj;
+      }
+    l_run += lsum;
+  };
+  auto seg_PV = [&](int t) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    const char* kb = smem + (t & (T::NSTAGE - 1)) * T::STAGE;
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          // the transpose hands lane l the keys 32kb2+16m2+8r+4(l/32)+e at d = 32db + l%32
+          const char* va = kb + voff[db] + (32 * kb2 + 16 * m2) * T::ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va + 8 * T::ROWB));
+          const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a32), pb[kb2][m2], o[db], 0, 0,
+                                                          0);
+        }
+      }
+    }
+  };
+
+  // prologue: tiles 0..2 in flight, S(0)
+  if (ntiles > 0) {
+    fetch_pages(t0);
+    gather_tile(0);
+    gather_tile(1);
+    gather_tile(2);
+    if (UNIFORM_PAGES && ntiles > 2)
+      __builtin_amdgcn_s_waitcnt(kWaitVm<4 * T::LOADS>);   // tile 0 landed (tiles 1, 2 may fly)
+    else if (UNIFORM_PAGES && ntiles > 1)
+      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * T::LOADS>);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (grp == 1) sync();   // group 1 runs one segment behind
+    seg_S(0);
+    sync();
+  }
+  // tile t: segments V(t) and M(t) = PV(t) + S(t+1). The gather of tile t+3 goes
+  // with slot 2t+2: group 1 issues it before its V segment, group 0 before its M
+  // segment (both just after the barrier that frees the stage). Group 1 skips
+  // the barrier after its very last segment, which balances its extra first one.
+  for (int t = 0; t < ntiles; ++t) {
+    const bool last = t + 1 >= ntiles;
+    if (grp == 1) gather_tile(t + 3);
+    seg_V(t);
+    sync();
+    if (grp == 0) gather_tile(t + 3);
+    seg_PV(t);
+    if (!last) seg_S(t + 1);
+    if (!last || grp == 0) sync();
   }
   if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
 
