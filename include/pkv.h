@@ -135,8 +135,9 @@ int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const 
  * Errors: PKV_ERR_INVALID_ARGUMENT (null pointers, batch < 1, negative
  * lengths, int32 overflow of the sums, Hq % Hkv != 0, page_size < 1,
  * num_pages < 1, decode_splits outside 0..PKV_MAX_SPLITS),
- * PKV_ERR_UNSUPPORTED (head_dim not 64/128, dtype unknown, G > 128, device
- * not gfx950), PKV_ERR_WORKSPACE (a buffer too small), PKV_ERR_HIP.
+ * PKV_ERR_UNSUPPORTED (head_dim not 64/128, dtype unknown, G > 128, one
+ * token row of a pool >= 2^24 bytes or one page > 2^31-1 bytes, device not
+ * gfx950), PKV_ERR_WORKSPACE (a buffer too small), PKV_ERR_HIP.
  */
 int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                           const pkv_shape* shape, int32_t window, int32_t decode_splits,

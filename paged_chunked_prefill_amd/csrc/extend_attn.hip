@@ -135,6 +135,8 @@ constexpr float kRescaleSlack = 8.f;
 // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
 constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4);
+// s_waitcnt lgkmcnt(0) alone (vmcnt 63 and expcnt 7 do not wait)
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's
 // bytes land at LDS address `lds` + 16 l. Issued as inline asm so that the
@@ -177,13 +179,30 @@ struct Bf16Tile {
   static __device__ int vswz(int r) { return 2 * (r & (CH / 2 - 1)); }
 };
 
-template <int D, bool UNIFORM_PAGES>
+// Issue order of the MFMA segment (see seg_M below): NPV steps of O^T += V^T P^T
+// followed by NS steps of S^T = K Q^T, each one MFMA whose A fragment was read
+// from LDS `Ahead` steps earlier. Pins that order in the scheduler: the first
+// reads, then per step the reads of step+Ahead and the step's MFMA.
+template <int ST, int NSTEP, int NPV, int AHEAD>
+__device__ __forceinline__ void pin_m_schedule() {
+  constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
+  if constexpr (ST == 0) {
+    constexpr int first = (AHEAD < NPV ? 2 * AHEAD : 2 * NPV + (AHEAD - NPV));
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, first, 0);
+  }
+  if constexpr (ST + AHEAD < NSTEP) __builtin_amdgcn_sched_group_barrier(kMaskDsRead, ST + AHEAD < NPV ? 2 : 1, 0);
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
+  if constexpr (ST + 1 < NSTEP) pin_m_schedule<ST + 1, NSTEP, NPV, AHEAD>();
+}
+
+template <int D, bool POW2_PAGES>
 __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
   const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char*)smem));
 
   const ItemView it = load_item(p);
+  if (it.q_count <= 0) return;   // (uniform) a malformed item covers no row
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -200,19 +219,6 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   const int qpos_first = it.prefix + it.q_begin;
   const int qpos_last = it.prefix + it.q_begin + it.q_count - 1;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7]
-  bf16x8 qf[T::KSTEPS];
-  {
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
-                                                       (int64_t(gtok) * p.num_q_heads + head) * D + 8 * half);
-#pragma unroll
-    for (int ks = 0; ks < T::KSTEPS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_live) v = qrow[2 * ks];
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
   f32x16 o[T::DBLK];
 #pragma unroll
   for (int db = 0; db < T::DBLK; ++db) o[db] = f32x16{};
@@ -225,8 +231,8 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   const char* kpool = static_cast<const char*>(p.k_pool);
   const char* vpool = static_cast<const char*>(p.v_pool);
   const int ps = p.page_size, ps_shift = p.page_shift;
-  const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * 2;
-  const uint32_t page_bytes = uint32_t(ps) * row_bytes;  // < 2^31, checked on the host
+  const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * 2;   // < 2^24, checked on the host
+  const uint32_t page_bytes = uint32_t(ps) * row_bytes;          // < 2^31, checked on the host
   const int kv_last = it.kv_end - 1;
 
   // Gather: wave w's copy i fills LDS rows RPI*(NW*i+w) .. +RPI-1 of a tile; lane l
@@ -234,47 +240,48 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // Both swizzles depend on the row only modulo CH, the same for every i. A key
   // outside [kv_begin, kv_end) reads the nearest key inside the range instead:
   // finite data that the mask turns into a -inf score and a zero weight, and no
-  // slot past the request's positions is ever touched. With UNIFORM_PAGES (the
-  // page size a multiple of RPI) the RPI rows of one copy share a page: its id
-  // is one scalar load (constant address space, so it never waits on copies in
-  // flight) and the source is a scalar base plus a 32-bit lane offset.
+  // slot past the request's positions is ever touched. With POW2_PAGES (a
+  // power-of-two page size of at least RPI rows) the RPI rows of one copy share
+  // a page, before and after that clamp: its id is one scalar load (constant
+  // address space, so it never waits on copies in flight) and the source is a
+  // scalar base plus a 32-bit lane offset.
   const int lrow = lane / T::CH;
   const int srow = T::RPI * wave + lrow;   // row modulo CH decides both swizzles
   const uint32_t src_k = uint32_t(it.kv_head) * D * 2 + 16 * ((lane % T::CH) ^ T::kswz(srow));
   const uint32_t src_v = uint32_t(it.kv_head) * D * 2 + 16 * ((lane % T::CH) ^ T::vswz(srow));
   auto clampk = [&](int j) __attribute__((always_inline)) { return min(max(j, it.kv_begin), kv_last); };
-  auto page_col = [&](int j) __attribute__((always_inline)) { return ps_shift >= 0 ? (j >> ps_shift) : j / ps; };
+  auto page_col = [&](int j) __attribute__((always_inline)) { return POW2_PAGES ? (j >> ps_shift) : j / ps; };
   const __attribute__((address_space(4))) int32_t* pt_const = (const __attribute__((address_space(4))) int32_t*)pt;
   int pg[T::LOADS];  // page ids for the next tile to gather
   bool bad_page = false;
-  auto fetch_pages = [&](int kv0) __attribute__((always_inline)) {
+  auto fetch_pages = [&](int* ids, int kv0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int blk = kv0 + T::RPI * (T::NW * i + wave);
-      if (UNIFORM_PAGES)
-        pg[i] = pt_const[page_col(clampk(blk))];
+      if (POW2_PAGES)
+        ids[i] = pt_const[page_col(clampk(blk))];
       else
-        pg[i] = pt[page_col(clampk(blk + lrow))];
+        ids[i] = pt[page_col(clampk(blk + lrow))];
     }
   };
-  auto gather = [&](int kv0, uint32_t stage_lds) __attribute__((always_inline)) {
+  auto gather = [&](const int* ids, int kv0, uint32_t stage_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int j = clampk(kv0 + T::RPI * (T::NW * i + wave) + lrow);
-      const int slot = ps_shift >= 0 ? (j & (ps - 1)) : j - (j / ps) * ps;
-      const int page = pg[i];
-      const bool ok = page >= 0 && page < p.num_pages;
+      const int page = ids[i];
+      const bool ok = uint32_t(page) < uint32_t(p.num_pages);
       bad_page |= !ok;
       const uint32_t dst = stage_lds + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this copy
-      const uint32_t off = uint32_t(slot) * row_bytes;
-      if (UNIFORM_PAGES) {
+      if (POW2_PAGES) {
+        const uint32_t off = __umul24(uint32_t(j & (ps - 1)), row_bytes);
         const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes;
         const char* kb = ok ? kpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
         const char* vb = ok ? vpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
         lds_copy16(kb, ok ? off + src_k : 16u * lane, dst);
         lds_copy16(vb, ok ? off + src_v : 16u * lane, dst + T::TILEB);
       } else {
-        const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes + off;
+        const int slot = j - (j / ps) * ps;
+        const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes + uint32_t(slot) * row_bytes;
         const char* zero = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
         lds_copy16(ok ? kpool + pbase + src_k : zero, dst);
         lds_copy16(ok ? vpool + pbase + src_v : zero, dst + T::TILEB);
@@ -310,22 +317,24 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // issued in slot 2u-4 (once both groups have read tile u-4 from that stage)
   // and must land before slot 2u, where group 0 first reads K(u). Every barrier
   // first waits for this wave's gathers older than the newest one, so a gather
-  // has about three slots to land.
+  // has about three slots to land. Page ids of the next tile to gather are
+  // loaded at the start of a V segment: it reads no LDS, so no LDS wait there
+  // has to wait for the scalar loads too (they share one counter).
   const int grp = wave >> 2;
   const float c = p.scale_log2;
   const int window = p.window;
   bool newest_issued = false;   // was the most recent gather slot a real tile?
 
-  auto gather_tile = [&](int u) __attribute__((always_inline)) {
+  auto gather_tile = [&](const int* ids, int u) __attribute__((always_inline)) {
     newest_issued = u < ntiles;
-    if (u < ntiles) {
-      gather(t0 + u * T::BC, lds0 + uint32_t(u & (T::NSTAGE - 1)) * T::STAGE);
-      if (u + 1 < ntiles) fetch_pages(t0 + (u + 1) * T::BC);
-    }
+    if (u < ntiles) gather(ids, t0 + u * T::BC, lds0 + uint32_t(u & (T::NSTAGE - 1)) * T::STAGE);
   };
-  // wait for LDS reads and for every gather but the newest, then the block barrier
+  // wait for LDS reads and for every gather but the newest, then the block barrier.
+  // The LDS/scalar wait comes first on its own so that it stays on every path
+  // (the compiler then knows no scalar load is pending after a barrier).
   auto sync = [&]() __attribute__((always_inline)) {
-    if (UNIFORM_PAGES && newest_issued)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (POW2_PAGES && newest_issued)
       __builtin_amdgcn_s_waitcnt(kWaitVm<2 * T::LOADS>);
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
@@ -334,23 +343,50 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     asm volatile("" ::: "memory");
   };
 
+  // prologue part 1: tiles 0..2 in flight; group 1 also holds the ids of tile 3
+  if (ntiles > 0) {
+    int pg1[T::LOADS], pg2[T::LOADS];
+    fetch_pages(pg, t0);
+    fetch_pages(pg1, t0 + T::BC);
+    fetch_pages(pg2, t0 + 2 * T::BC);
+    gather_tile(pg, 0);
+    gather_tile(pg1, 1);
+    gather_tile(pg2, 2);
+    if (grp == 1 && 3 < ntiles) fetch_pages(pg, t0 + 3 * T::BC);
+  }
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7].
+  // Rows past the tile read the tile's first token (finite, never stored), so
+  // every lane loads and the loads are complete on every path after the wait
+  // below: no later instruction ever has to wait for them (such a wait would
+  // also wait for the gathers in flight).
+  bf16x8 qf[T::KSTEPS];
+  {
+    const int qtok = row_live ? gtok : it.qo + it.q_begin;
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
+                                                       (int64_t(qtok) * p.num_q_heads + head) * D + 8 * half);
+#pragma unroll
+    for (int ks = 0; ks < T::KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qrow[2 * ks]);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // Q, tiles 0..2 landed
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
   f32x16 s[2];            // scores S^T of the tile in flight (two 32-key blocks)
   bf16x8 pb[2][2];        // P of the tile being accumulated, as B operands
-  auto seg_S = [&](int u) __attribute__((always_inline)) {
-    if (!wave_live) return;
-    const char* kb = smem + (u & (T::NSTAGE - 1)) * T::STAGE;
+  auto k_frag = [&](uint32_t kb, int ks, int kb2) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(smem + kb + koff[ks] + 32 * kb2 * T::ROWB);
+  };
+  auto seg_S0 = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       s[kb2] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < T::KSTEPS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + koff[ks] + 32 * kb2 * T::ROWB);
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
-      }
+      for (int ks = 0; ks < T::KSTEPS; ++ks)
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(0, ks, kb2), qf[ks], s[kb2], 0, 0, 0);
     }
   };
   auto seg_V = [&](int t) __attribute__((always_inline)) {
-    if (!wave_live) return;
     const int kv0 = t0 + t * T::BC;
     // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
     const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
@@ -398,46 +434,53 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       }
     l_run += lsum;
   };
-  auto seg_PV = [&](int t) __attribute__((always_inline)) {
-    if (!wave_live) return;
-    const char* kb = smem + (t & (T::NSTAGE - 1)) * T::STAGE;
+  // segment M: O += V(t)^T P(t) then S(t+1) = K(t+1) Q^T, as one straight run of
+  // MFMAs. Step i (< NPV) is the PV product of d-block i % DBLK with key quarter
+  // i / DBLK; step NPV + 2ks + kb2 is the S product of k-step ks with key block
+  // kb2. Consecutive MFMAs accumulate into different registers, and each A
+  // fragment is read from LDS AHEAD steps before its MFMA. After the last tile
+  // the S half reads a stale stage whose result is never used.
+  constexpr int NPV = 4 * T::DBLK, NSTEP = NPV + 2 * T::KSTEPS, AHEAD = 4;
+  auto seg_M = [&](int t) __attribute__((always_inline)) {
+    const uint32_t vst = uint32_t(t & (T::NSTAGE - 1)) * T::STAGE;
+    const uint32_t kst = uint32_t((t + 1) & (T::NSTAGE - 1)) * T::STAGE;
+    auto frag = [&](int st) __attribute__((always_inline)) {
+      if (st < NPV) {
+        const int db = st % T::DBLK, km = st / T::DBLK;
+        // the transpose hands lane l the keys 16km+8r+4(l/32)+e at d = 32db + l%32
+        const char* va = smem + vst + voff[db] + 16 * km * T::ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va + 8 * T::ROWB));
+        const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
+        return __builtin_bit_cast(bf16x8, a32);
+      }
+      const int ks = (st - NPV) >> 1, kb2 = (st - NPV) & 1;
+      return k_frag(kst, ks, kb2);
+    };
+    bf16x8 fr[AHEAD];
 #pragma unroll
-    for (int db = 0; db < T::DBLK; ++db) {
+    for (int st = 0; st < AHEAD; ++st) fr[st] = frag(st);
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-          // the transpose hands lane l the keys 32kb2+16m2+8r+4(l/32)+e at d = 32db + l%32
-          const char* va = kb + voff[db] + (32 * kb2 + 16 * m2) * T::ROWB;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
-          const i16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va + 8 * T::ROWB));
-          const u32x2 lo32 = __builtin_bit_cast(u32x2, lo), hi32 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a32), pb[kb2][m2], o[db], 0, 0,
-                                                          0);
-        }
+    for (int st = 0; st < NSTEP; ++st) {
+      const bf16x8 a = fr[st % AHEAD];
+      if (st + AHEAD < NSTEP) fr[st % AHEAD] = frag(st + AHEAD);
+      if (st < NPV) {
+        const int db = st % T::DBLK, km = st / T::DBLK;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[km >> 1][km & 1], o[db], 0, 0, 0);
+      } else {
+        const int ks = (st - NPV) >> 1, kb2 = (st - NPV) & 1;
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : s[kb2], 0, 0, 0);
       }
     }
+    pin_m_schedule<0, NSTEP, NPV, AHEAD>();
   };
 
-  // prologue: tiles 0..2 in flight, S(0)
+  // prologue part 2: S(0), group 1 one segment behind
   if (ntiles > 0) {
-    fetch_pages(t0);
-    gather_tile(0);
-    gather_tile(1);
-    gather_tile(2);
-    if (UNIFORM_PAGES && ntiles > 2)
-      __builtin_amdgcn_s_waitcnt(kWaitVm<4 * T::LOADS>);   // tile 0 landed (tiles 1, 2 may fly)
-    else if (UNIFORM_PAGES && ntiles > 1)
-      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * T::LOADS>);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (grp == 1) sync();   // group 1 runs one segment behind
-    seg_S(0);
+    if (grp == 1) sync();
+    if (wave_live) seg_S0();
     sync();
   }
   // tile t: segments V(t) and M(t) = PV(t) + S(t+1). The gather of tile t+3 goes
@@ -446,12 +489,12 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // the barrier after its very last segment, which balances its extra first one.
   for (int t = 0; t < ntiles; ++t) {
     const bool last = t + 1 >= ntiles;
-    if (grp == 1) gather_tile(t + 3);
-    seg_V(t);
+    if (grp == 1) gather_tile(pg, t + 3);
+    if (t + 3 + grp < ntiles) fetch_pages(pg, t0 + (t + 3 + grp) * T::BC);   // next gather of this group
+    if (wave_live) seg_V(t);
     sync();
-    if (grp == 0) gather_tile(t + 3);
-    seg_PV(t);
-    if (!last) seg_S(t + 1);
+    if (grp == 0) gather_tile(pg, t + 3);
+    if (wave_live) seg_M(t);
     if (!last || grp == 0) sync();
   }
   if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
@@ -733,8 +776,10 @@ template <int D, bool BF16>
 void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
   if (a.n_items > 0) {
     if (BF16) {
-      // the rows of one wave-wide gather share a page when the page size is a multiple of them
-      if (a.shape.page_size % Bf16Tile<D>::RPI == 0)
+      // the rows of one wave-wide gather share a page when the page size is a
+      // power of two of at least that many rows
+      const int ps = a.shape.page_size;
+      if ((ps & (ps - 1)) == 0 && ps >= Bf16Tile<D>::RPI)
         hipLaunchKernelGGL((extend_attn_bf16<D, true>), dim3(a.n_items), dim3(64 * kWavesBf16), 0, st, p);
       else
         hipLaunchKernelGGL((extend_attn_bf16<D, false>), dim3(a.n_items), dim3(64 * kWavesBf16), 0, st, p);

@@ -35,6 +35,10 @@ int validate_shape(const pkv_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128)
     return set_error(PKV_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", s->head_dim);
   const int64_t page_bytes = int64_t(s->page_size) * s->num_kv_heads * s->head_dim * (s->dtype == PKV_DTYPE_BF16 ? 2 : 4);
+  const int64_t row_bytes = page_bytes / s->page_size;
+  if (row_bytes >= (int64_t(1) << 24))
+    return set_error(PKV_ERR_UNSUPPORTED, "one token row of one pool spans %lld bytes (at most 2^24-1 supported)",
+                     (long long)row_bytes);
   if (page_bytes > INT32_MAX)
     return set_error(PKV_ERR_UNSUPPORTED, "one page of one pool spans %lld bytes (at most 2^31-1 supported)",
                      (long long)page_bytes);
