@@ -149,13 +149,13 @@ __device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uin
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
+               : "m0");
 }
 __device__ __forceinline__ void lds_copy16(const void* vaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(vaddr), "s"(lds)
-               : "memory", "m0");
+               : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -172,27 +172,35 @@ struct Bf16Tile {
   static constexpr int LOADS = BC / RPI / NW;    // such copies per wave per tensor and tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
-  // K rows: chunk c of row r lives at chunk c ^ (r mod CH) -> the 32 rows of a
-  // b128 read spread over all banks. V rows: chunk c at c ^ 2(r mod CH/2),
-  // which keeps chunk pairs adjacent for the 8-byte transposing reads.
-  static __device__ int kswz(int r) { return r & (CH - 1); }
-  static __device__ int vswz(int r) { return 2 * (r & (CH / 2 - 1)); }
+  // XOR swizzles of the 16-byte chunks of a row (64 banks of 4 bytes = 256 B
+  // per bank row; a D=64 row is half of one). K: the 16 lanes of a b128 read
+  // that issue together read 16 rows at one chunk index; chunk c of row r sits
+  // at c ^ (r mod 16) for D=128, at c ^ ((r/2) mod 8) for D=64, so they cover
+  // all 64 banks. V: a half-wave of transposing reads takes 64 bytes (a group
+  // of 4 chunks) from each of 4 consecutive rows; the group index is XORed with
+  // r mod 4 (D=128) or (r/2) mod 2 (D=64) so the 4 rows use disjoint banks.
+  // K's depends on r modulo 16 and V's on r modulo 4; the row offsets added
+  // to a lane's base row (multiples of 32 for K, of 8 for V) keep them.
+  static __device__ int kswz(int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ int vswz(int r) { return CH == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// Issue order of the MFMA segment (see seg_M below): NPV steps of O^T += V^T P^T
-// followed by NS steps of S^T = K Q^T, each one MFMA whose A fragment was read
-// from LDS `Ahead` steps earlier. Pins that order in the scheduler: the first
-// reads, then per step the reads of step+Ahead and the step's MFMA.
-template <int ST, int NSTEP, int NPV, int AHEAD>
+// Issue order of the MFMA segment (see seg_M below): PV and S steps
+// alternate (even steps PV, odd steps S), each one MFMA whose A fragment was
+// read from LDS AHEAD steps earlier (two transposing reads for PV, one b128 read
+// for S). Pins that order in the scheduler: the first reads, then per step the
+// reads of step+AHEAD and the step's MFMA.
+template <int ST, int NSTEP, int AHEAD>
 __device__ __forceinline__ void pin_m_schedule() {
   constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
   if constexpr (ST == 0) {
-    constexpr int first = (AHEAD < NPV ? 2 * AHEAD : 2 * NPV + (AHEAD - NPV));
+    constexpr int first = AHEAD + (AHEAD + 1) / 2;   // 2 reads per even step, 1 per odd step
     __builtin_amdgcn_sched_group_barrier(kMaskDsRead, first, 0);
   }
-  if constexpr (ST + AHEAD < NSTEP) __builtin_amdgcn_sched_group_barrier(kMaskDsRead, ST + AHEAD < NPV ? 2 : 1, 0);
+  if constexpr (ST + AHEAD < NSTEP)
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, (ST + AHEAD) % 2 == 0 ? 2 : 1, 0);
   __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
-  if constexpr (ST + 1 < NSTEP) pin_m_schedule<ST + 1, NSTEP, NPV, AHEAD>();
+  if constexpr (ST + 1 < NSTEP) pin_m_schedule<ST + 1, NSTEP, AHEAD>();
 }
 
 template <int D, bool POW2_PAGES>
@@ -264,28 +272,45 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
         ids[i] = pt[page_col(clampk(blk + lrow))];
     }
   };
-  auto gather = [&](const int* ids, int kv0, uint32_t stage_lds) __attribute__((always_inline)) {
+  // One wave-wide copy of RPI key rows of K and of V: with POW2_PAGES a scalar
+  // base and a lane offset each, else a full lane address each.
+  struct Copy {
+    const char* k;
+    const char* v;
+    uint32_t koff, voff, dst;
+  };
+  auto prepare = [&](const int* ids, int kv0, uint32_t stage_lds, Copy* cp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int j = clampk(kv0 + T::RPI * (T::NW * i + wave) + lrow);
       const int page = ids[i];
       const bool ok = uint32_t(page) < uint32_t(p.num_pages);
       bad_page |= !ok;
-      const uint32_t dst = stage_lds + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this copy
+      cp[i].dst = stage_lds + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this copy
       if (POW2_PAGES) {
         const uint32_t off = __umul24(uint32_t(j & (ps - 1)), row_bytes);
         const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes;
-        const char* kb = ok ? kpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
-        const char* vb = ok ? vpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
-        lds_copy16(kb, ok ? off + src_k : 16u * lane, dst);
-        lds_copy16(vb, ok ? off + src_v : 16u * lane, dst + T::TILEB);
+        cp[i].k = ok ? kpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
+        cp[i].v = ok ? vpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
+        cp[i].koff = ok ? off + src_k : 16u * lane;
+        cp[i].voff = ok ? off + src_v : 16u * lane;
       } else {
         const int slot = j - (j / ps) * ps;
         const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes + uint32_t(slot) * row_bytes;
         const char* zero = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
-        lds_copy16(ok ? kpool + pbase + src_k : zero, dst);
-        lds_copy16(ok ? vpool + pbase + src_v : zero, dst + T::TILEB);
+        cp[i].k = ok ? kpool + pbase + src_k : zero;
+        cp[i].v = ok ? vpool + pbase + src_v : zero;
+        cp[i].koff = cp[i].voff = 0;
       }
+    }
+  };
+  // copy c of a prepared tile: K rows for even c, V rows for odd c
+  auto issue = [&](const Copy* cp, int c) __attribute__((always_inline)) {
+    const Copy& x = cp[c >> 1];
+    if (POW2_PAGES) {
+      if (c & 1) lds_copy16(x.v, x.voff, x.dst + T::TILEB); else lds_copy16(x.k, x.koff, x.dst);
+    } else {
+      if (c & 1) lds_copy16(x.v, x.dst + T::TILEB); else lds_copy16(x.k, x.dst);
     }
   };
 
@@ -317,17 +342,17 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // issued in slot 2u-4 (once both groups have read tile u-4 from that stage)
   // and must land before slot 2u, where group 0 first reads K(u). Every barrier
   // first waits for this wave's gathers older than the newest one, so a gather
-  // has about three slots to land. Page ids of the next tile to gather are
-  // loaded at the start of a V segment: it reads no LDS, so no LDS wait there
-  // has to wait for the scalar loads too (they share one counter).
+  // has about three slots to land. Each wave loads the page ids of tile t+3 at
+  // the start of its V(t) segment (it reads no LDS, so no LDS wait there has to
+  // wait for the scalar loads too: they share one counter) and issues its copies
+  // of tile t+3 spread over its M(t) segment, between the MFMAs.
   const int grp = wave >> 2;
   const float c = p.scale_log2;
   const int window = p.window;
-  bool newest_issued = false;   // was the most recent gather slot a real tile?
-
-  auto gather_tile = [&](const int* ids, int u) __attribute__((always_inline)) {
-    newest_issued = u < ntiles;
-    if (u < ntiles) gather(ids, t0 + u * T::BC, lds0 + uint32_t(u & (T::NSTAGE - 1)) * T::STAGE);
+  bool newest_issued = false;   // was the most recent gather real (or a clamped one)?
+  Copy cp[T::LOADS];
+  auto stage_of = [&](int u) __attribute__((always_inline)) {
+    return lds0 + uint32_t(u & (T::NSTAGE - 1)) * T::STAGE;
   };
   // wait for LDS reads and for every gather but the newest, then the block barrier.
   // The LDS/scalar wait comes first on its own so that it stays on every path
@@ -343,16 +368,20 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     asm volatile("" ::: "memory");
   };
 
-  // prologue part 1: tiles 0..2 in flight; group 1 also holds the ids of tile 3
+  // prologue part 1: tiles 0..2 in flight
   if (ntiles > 0) {
-    int pg1[T::LOADS], pg2[T::LOADS];
-    fetch_pages(pg, t0);
-    fetch_pages(pg1, t0 + T::BC);
-    fetch_pages(pg2, t0 + 2 * T::BC);
-    gather_tile(pg, 0);
-    gather_tile(pg1, 1);
-    gather_tile(pg2, 2);
-    if (grp == 1 && 3 < ntiles) fetch_pages(pg, t0 + 3 * T::BC);
+    int ids[3][T::LOADS];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) fetch_pages(ids[u], t0 + u * T::BC);
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      if (u < ntiles) {
+        prepare(ids[u], t0 + u * T::BC, stage_of(u), cp);
+#pragma unroll
+        for (int c2 = 0; c2 < 2 * T::LOADS; ++c2) issue(cp, c2);
+      }
+    }
+    newest_issued = ntiles > 2;
   }
   // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7].
   // Rows past the tile read the tile's first token (finite, never stored), so
@@ -434,19 +463,25 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       }
     l_run += lsum;
   };
-  // segment M: O += V(t)^T P(t) then S(t+1) = K(t+1) Q^T, as one straight run of
-  // MFMAs. Step i (< NPV) is the PV product of d-block i % DBLK with key quarter
-  // i / DBLK; step NPV + 2ks + kb2 is the S product of k-step ks with key block
-  // kb2. Consecutive MFMAs accumulate into different registers, and each A
-  // fragment is read from LDS AHEAD steps before its MFMA. After the last tile
-  // the S half reads a stale stage whose result is never used.
-  constexpr int NPV = 4 * T::DBLK, NSTEP = NPV + 2 * T::KSTEPS, AHEAD = 4;
+  // segment M: O += V(t)^T P(t) and S(t+1) = K(t+1) Q^T, as one straight run of
+  // MFMAs. Even step 2i is PV product i (d-block i % DBLK, key quarter i / DBLK),
+  // odd step 2i+1 is S product i (k-step i / 2, key block i % 2): an MFMA that
+  // accumulates into the registers of an earlier one comes 4 or more MFMAs
+  // after it, past its latency. Each A fragment is read from LDS AHEAD steps
+  // before its MFMA (at most 6 reads in flight; the LDS counter tracks 15).
+  // After the last tile the S products read a stale stage and are never used.
+  static_assert(4 * T::DBLK == 2 * T::KSTEPS, "PV and S steps pair up");
+  constexpr int NSTEP = 8 * T::DBLK, AHEAD = 4;
+  // the copies of a gather go out at these steps, spread over the segment
+  constexpr int NCOPY = 2 * T::LOADS, COPY_GAP = NSTEP / NCOPY;
   auto seg_M = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);   // MFMA issue first when the SIMD's other wave is in its V segment
     const uint32_t vst = uint32_t(t & (T::NSTAGE - 1)) * T::STAGE;
     const uint32_t kst = uint32_t((t + 1) & (T::NSTAGE - 1)) * T::STAGE;
     auto frag = [&](int st) __attribute__((always_inline)) {
-      if (st < NPV) {
-        const int db = st % T::DBLK, km = st / T::DBLK;
+      const int i = st >> 1;
+      if ((st & 1) == 0) {
+        const int db = i % T::DBLK, km = i / T::DBLK;
         // the transpose hands lane l the keys 16km+8r+4(l/32)+e at d = 32db + l%32
         const char* va = smem + vst + voff[db] + 16 * km * T::ROWB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(va));
@@ -456,8 +491,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
         const u32x4 a32 = {lo32[0], lo32[1], hi32[0], hi32[1]};
         return __builtin_bit_cast(bf16x8, a32);
       }
-      const int ks = (st - NPV) >> 1, kb2 = (st - NPV) & 1;
-      return k_frag(kst, ks, kb2);
+      return k_frag(kst, i >> 1, i & 1);
     };
     bf16x8 fr[AHEAD];
 #pragma unroll
@@ -466,15 +500,18 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     for (int st = 0; st < NSTEP; ++st) {
       const bf16x8 a = fr[st % AHEAD];
       if (st + AHEAD < NSTEP) fr[st % AHEAD] = frag(st + AHEAD);
-      if (st < NPV) {
-        const int db = st % T::DBLK, km = st / T::DBLK;
+      if (st % COPY_GAP == 2) issue(cp, st / COPY_GAP);
+      const int i = st >> 1;
+      if ((st & 1) == 0) {
+        const int db = i % T::DBLK, km = i / T::DBLK;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[km >> 1][km & 1], o[db], 0, 0, 0);
       } else {
-        const int ks = (st - NPV) >> 1, kb2 = (st - NPV) & 1;
+        const int ks = i >> 1, kb2 = i & 1;
         s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : s[kb2], 0, 0, 0);
       }
     }
-    pin_m_schedule<0, NSTEP, NPV, AHEAD>();
+    pin_m_schedule<0, NSTEP, AHEAD>();
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // prologue part 2: S(0), group 1 one segment behind
@@ -487,16 +524,25 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // with slot 2t+2: group 1 issues it before its V segment, group 0 before its M
   // segment (both just after the barrier that frees the stage). Group 1 skips
   // the barrier after its very last segment, which balances its extra first one.
+  // Past the last tile the gathers still run, of keys clamped to the last one
+  // (in bounds, mostly one repeated row) into stages that are no longer read,
+  // which keeps the segment free of branches; they are waited for below.
+  newest_issued = true;
   for (int t = 0; t < ntiles; ++t) {
     const bool last = t + 1 >= ntiles;
-    if (grp == 1) gather_tile(pg, t + 3);
-    if (t + 3 + grp < ntiles) fetch_pages(pg, t0 + (t + 3 + grp) * T::BC);   // next gather of this group
+    fetch_pages(pg, t0 + (t + 3) * T::BC);
     if (wave_live) seg_V(t);
+    prepare(pg, t0 + (t + 3) * T::BC, stage_of(t + 3), cp);   // addresses only: nothing is written yet
     sync();
-    if (grp == 0) gather_tile(pg, t + 3);
-    if (wave_live) seg_M(t);
+    if (wave_live) {
+      seg_M(t);
+    } else {
+#pragma unroll
+      for (int c2 = 0; c2 < NCOPY; ++c2) issue(cp, c2);
+    }
     if (!last || grp == 0) sync();
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // no copy into LDS outlives the workgroup
   if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
 
   if (!wave_live) return;
