@@ -169,9 +169,10 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   // ---- KV splits.
   // One-token rows: the explicit count, or enough splits to give the GPU about
   // two items per compute unit. Prefill tiles: when the launch has fewer items
-  // than resident workgroup slots, the longest tiles are cut into key ranges of
-  // roughly equal cost so every slot gets work; a tile's cost is its 64-key
-  // blocks times its live 32-row waves.
+  // than resident workgroup slots, tiles are cut into key ranges so that the
+  // launch has at most one item per slot (a second round of items would double
+  // the time of the slots that run it) with the largest item as small as that
+  // allows; a tile's cost is its 64-key blocks times its live 32-row waves.
   auto granules_of = [](const Tile& t) {
     return std::max(1, ceil_div(t.kv_hi, kSplitGranule) - t.kv_lo / kSplitGranule);
   };
@@ -187,7 +188,33 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   if (decode_splits == 0 && n_one > 0 && base_items > 0)
     auto_splits = std::min<int32_t>(PKV_MAX_SPLITS, std::max<int32_t>(1, ceil_div(2LL * num_cus, base_items)));
   const int64_t slots = int64_t(num_cus) * slots_per_cu(shape->dtype);
-  const int64_t unit = base_items < slots ? std::max<int64_t>(1, (total_cost + slots - 1) / slots) : 0;
+  auto prefill_cap = [&](const Tile& t) {
+    return std::min<int64_t>(kMaxPrefillSplits, std::max(1, granules_of(t) / 2));
+  };
+  auto one_token_splits = [&](const Tile& t) {
+    return decode_splits > 0 ? std::min(decode_splits, granules_of(t))
+                             : std::min(auto_splits, std::max(1, granules_of(t) / 2));
+  };
+  // items of the launch when every prefill tile is cut into pieces of cost <= u
+  auto items_at = [&](int64_t u) {
+    int64_t n = 0;
+    for (const Tile& t : tiles) {
+      const int64_t c = int64_t(granules_of(t)) * waves_of(t);
+      n += int64_t(hkv) * (t.one_token ? one_token_splits(t) : std::min(prefill_cap(t), (c + u - 1) / u));
+    }
+    return n;
+  };
+  int64_t unit = 0;  // 0: prefill tiles stay whole
+  if (base_items < slots) {
+    int64_t lo = 1, hi = 1;
+    for (const Tile& t : tiles) hi = std::max<int64_t>(hi, int64_t(granules_of(t)) * waves_of(t));
+    // smallest piece cost whose item count fits the slots (counts fall as u grows)
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (items_at(mid) <= slots) hi = mid; else lo = mid + 1;
+    }
+    unit = lo;
+  }
 
   std::vector<WorkItem> items;
   std::vector<int32_t> split_rows;  // pairs (token, splits)
@@ -197,14 +224,10 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     const int32_t granules = granules_of(t);
     int32_t splits = 1;
     if (t.one_token) {
-      if (decode_splits > 0)
-        splits = std::min(decode_splits, granules);
-      else
-        splits = std::min(auto_splits, std::max(1, granules / 2));
+      splits = one_token_splits(t);
     } else if (unit > 0) {
       const int64_t want = (int64_t(granules) * waves_of(t) + unit - 1) / unit;
-      splits = int32_t(std::min<int64_t>({want, kMaxPrefillSplits, std::max(1, granules / 2)}));
-      splits = std::max(splits, 1);
+      splits = int32_t(std::max<int64_t>(1, std::min(want, prefill_cap(t))));
     }
     int32_t part_row = -1;
     if (splits > 1) {
