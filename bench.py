@@ -29,6 +29,9 @@ for _p in (ROOT, os.path.join(ROOT, "tests")):
         sys.path.insert(0, _p)
 
 METRIC = "extend-attn TFLOP/s + % bf16 MFMA peak (4097-tok prompt, 512 chunk), tokens/s"
+KERNEL_SRC = os.path.join(ROOT, "paged_chunked_prefill_amd", "csrc", "extend_attn.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 256 << 20       # bytes read and written per copy_calibration launch
 MFMA_PEAK_BF16 = 2500.0      # TFLOP/s, MI355X dense bf16
 MFMA_PEAK_FP32 = 157.3       # TFLOP/s, MI355X fp32 matrix (vector figure as stated for the chip)
 HBM_PEAK = 8000.0            # GB/s
@@ -95,7 +98,16 @@ def main():
     ap.add_argument("--workload", default="prompt4097_chunk512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows for the CPU oracle sample (0: auto)")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE of --workload; the same "
+                         "two of copy_calibration): print the attention kernel's HBM traffic per launch as JSON")
     args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args)
+    if args.summarize_traffic:
+        return summarize_traffic(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -207,6 +219,13 @@ def main():
         "algorithmic_per_launch": round((hbm_bytes if decode_bound else flops) / n_launch),
     }
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+    tr = load_traffic(args.workload)
+    if tr is not None:
+        # HBM bytes per attention kernel launch from the FETCH_SIZE / WRITE_SIZE counters, scaled by the
+        # same counters on a copy of known size; the split combine's bytes are not in it
+        roofline["traffic"] = tr["traffic_bytes_per_launch"]
+        roofline["traffic_vs_algorithmic_bytes"] = round(tr["traffic_bytes_per_launch"] / (hbm_bytes / n_launch), 3)
+        roofline["traffic_source"] = f"profiles/traffic_{args.workload}.json"
 
     # check the last step's outputs are finite (no canary NaN reached the result)
     for b in B:
@@ -231,6 +250,68 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "setup_s": round(setup_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def kernel_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(name):
+    """Counter traffic recorded for this workload, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    return tr if tr.get("kernel_source_sha256_16") == kernel_hash() else None
+
+
+def _counter_means(directory, match):
+    """Counter values summed over the instances of each dispatch whose kernel name contains `match`,
+    then averaged over those dispatches (rocprofv3 csv: run_counter_collection.csv)."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    with open(os.path.join(directory, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if match in r["Kernel_Name"]:
+                per[(r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
+    out = collections.defaultdict(list)
+    for (_, c), v in per.items():
+        out[c].append(v)
+    return {c: sum(v) / len(v) for c, v in out.items()}, len({d for d, _ in per})
+
+
+def summarize_traffic(args):
+    f_dir, w_dir, cf_dir, cw_dir = args.summarize_traffic
+    fetch, n = _counter_means(f_dir, "extend_attn")
+    write, _ = _counter_means(w_dir, "extend_attn")
+    cal_f, _ = _counter_means(cf_dir, "copyBuffer")
+    cal_w, _ = _counter_means(cw_dir, "copyBuffer")
+    fs = (COPY_BYTES / 1024) / cal_f["FETCH_SIZE"]    # counters are in KiB
+    ws = (COPY_BYTES / 1024) / cal_w["WRITE_SIZE"]
+    out = {"workload": args.workload, "kernel": "extend_attn", "kernel_source_sha256_16": kernel_hash(),
+           "dispatches": n, "fetch_kib_per_launch": round(fetch["FETCH_SIZE"], 1),
+           "write_kib_per_launch": round(write["WRITE_SIZE"], 1),
+           "copy_fetch_kib": round(cal_f["FETCH_SIZE"], 1), "copy_write_kib": round(cal_w["WRITE_SIZE"], 1),
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "traffic_bytes_per_launch": round((fetch["FETCH_SIZE"] * fs + write["WRITE_SIZE"] * ws) * 1024)}
+    print(json.dumps(out, indent=1))
+
+
+def summarize_stats(args):
+    import csv
+    with open(os.path.join(args.summarize_stats, "run_kernel_stats.csv")) as f:
+        rows = list(csv.DictReader(f))
+    print("| kernel | calls | total us | avg us | min us | max us | % of GPU time |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        print(f"| `{name[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+              f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.1f} |")
 
 
 def copy_calibration(args):
