@@ -62,40 +62,57 @@ int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
 // than XCDs.
 template <class Cost>
 std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
-  std::vector<WorkItem> items = in;
-  std::stable_sort(items.begin(), items.end(),
-                   [&](const WorkItem& a, const WorkItem& b) { return cost(a) > cost(b); });
-  const size_t n = items.size();
-  if (n < size_t(kXcds) * 2) return items;
-  // locality groups: items with equal (request, KV head, split)
-  auto key = [](const WorkItem& a) { return std::make_tuple(a.req, a.kv_head, a.split); };
-  std::vector<uint32_t> by_key(n);
-  for (size_t i = 0; i < n; ++i) by_key[i] = uint32_t(i);
-  std::stable_sort(by_key.begin(), by_key.end(),
-                   [&](uint32_t a, uint32_t b) { return key(items[a]) < key(items[b]); });
+  const size_t n = in.size();
+  std::vector<int64_t> c(n);
+  for (size_t i = 0; i < n; ++i) c[i] = cost(in[i]);
+  // Longest first, ties in the planner's order: one integer sort of
+  // (max cost - cost, index) packed into 64 bits (costs < 2^31 per item).
+  const int64_t cmax = n ? *std::max_element(c.begin(), c.end()) : 0;
+  std::vector<uint64_t> packed(n);
+  for (size_t i = 0; i < n; ++i) packed[i] = (uint64_t(cmax - c[i]) << 32) | uint64_t(i);
+  std::sort(packed.begin(), packed.end());
+  std::vector<uint32_t> ord(n);
+  for (size_t i = 0; i < n; ++i) ord[i] = uint32_t(packed[i] & 0xffffffffu);
+  std::vector<WorkItem> out;
+  out.reserve(n);
+  if (n < size_t(kXcds) * 2) {
+    for (uint32_t i : ord) out.push_back(in[i]);
+    return out;
+  }
+  // locality groups: items with equal (request, KV head, split); the packed key
+  // is exact because KV heads < 2^24 (a token row is < 2^24 bytes) and splits <= 32
+  std::vector<std::pair<uint64_t, uint32_t>> keyed(n);
+  for (size_t i = 0; i < n; ++i)
+    keyed[i] = {(uint64_t(uint32_t(in[i].req)) << 32) | (uint64_t(uint32_t(in[i].kv_head)) << 8) |
+                    uint64_t(uint32_t(in[i].split) & 0xff),
+                uint32_t(i)};
+  std::sort(keyed.begin(), keyed.end());
   std::vector<uint32_t> group_of(n);
   std::vector<int64_t> group_cost;
   for (size_t k = 0; k < n; ++k) {
-    if (k == 0 || key(items[by_key[k]]) != key(items[by_key[k - 1]])) group_cost.push_back(0);
-    group_of[by_key[k]] = uint32_t(group_cost.size() - 1);
-    group_cost.back() += cost(items[by_key[k]]);
+    if (k == 0 || keyed[k].first != keyed[k - 1].first) group_cost.push_back(0);
+    group_of[keyed[k].second] = uint32_t(group_cost.size() - 1);
+    group_cost.back() += c[keyed[k].second];
   }
-  std::vector<uint32_t> groups(group_cost.size());
-  for (size_t g = 0; g < groups.size(); ++g) groups[g] = uint32_t(g);
-  std::stable_sort(groups.begin(), groups.end(), [&](uint32_t a, uint32_t b) { return group_cost[a] > group_cost[b]; });
+  // groups to XCDs: largest first, each to the least-loaded XCD
+  const size_t ng = group_cost.size();
+  const int64_t gmax = *std::max_element(group_cost.begin(), group_cost.end());
+  std::vector<uint64_t> gpacked(ng);
+  for (size_t g = 0; g < ng; ++g) gpacked[g] = (uint64_t(gmax - group_cost[g]) << 32) | uint64_t(g);
+  std::sort(gpacked.begin(), gpacked.end());
   int64_t load[kXcds] = {};
   std::vector<uint8_t> xcd_of(group_cost.size());
-  for (uint32_t g : groups) {
+  for (uint64_t gp : gpacked) {
+    const uint32_t g = uint32_t(gp & 0xffffffffu);
     int best = 0;
     for (int x = 1; x < kXcds; ++x)
       if (load[x] < load[best]) best = x;
     load[best] += group_cost[g];
     xcd_of[g] = uint8_t(best);
   }
-  std::vector<std::vector<uint32_t>> per(kXcds);
-  for (size_t i = 0; i < n; ++i) per[xcd_of[group_of[i]]].push_back(uint32_t(i));  // keeps cost order
-  std::vector<WorkItem> out;
-  out.reserve(n);
+  // per-XCD lists in longest-first order, then dealt out round-robin
+  std::vector<uint32_t> per[kXcds];
+  for (uint32_t i : ord) per[xcd_of[group_of[i]]].push_back(i);
   size_t next[kXcds] = {};
   for (size_t i = 0; out.size() < n; ++i) {
     int x = int(i % kXcds);
@@ -106,7 +123,7 @@ std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
         if (next[y] < per[y].size() && (best < 0 || per[y].size() - next[y] > per[best].size() - next[best])) best = y;
       x = best;
     }
-    out.push_back(items[per[x][next[x]++]]);
+    out.push_back(in[per[x][next[x]++]]);
   }
   return out;
 }
@@ -217,6 +234,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   }
 
   std::vector<WorkItem> items;
+  items.reserve(size_t(base_items) * 2);
   std::vector<int32_t> split_rows;  // pairs (token, splits)
   int32_t n_split_rows = 0, max_splits = 1;
   for (const Tile& t : tiles) {
