@@ -768,53 +768,66 @@ struct CombineParams {
   int32_t total_q;
 };
 
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+// One row of 32 lanes per (split row, query head), two rows per wave: each
+// lane owns VEC = D/32 consecutive output values and loads them with one
+// 8- or 16-byte read per split. Lane j < ns of a row also holds split j's
+// (max, sum); 32 lanes cover every split count a plan can have.
+template <int D>
+struct CombineShape {
+  static constexpr int LANES = 32;
+  static constexpr int ROWS = 2;
+  static constexpr int VEC = D / 32;
+  static_assert(PKV_MAX_SPLITS <= LANES, "one lane per split");
+};
 
-// One wave per (split row, query head): lane k holds split k's (max, sum); the
-// output loop then issues every split's partial loads back to back.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  using C = CombineShape<D>;
+  typedef float fvec __attribute__((ext_vector_type(C::VEC)));
   const int lane = threadIdx.x & 63;
-  if (wid >= p.n_rows) return;
-  const int slot = wid / p.num_q_heads, head = wid - slot * p.num_q_heads;
+  const int sub = lane / C::LANES, j = lane % C::LANES;      // row within the wave, lane within the row
+  const int wid = (blockIdx.x * 4 + (threadIdx.x >> 6)) * C::ROWS + sub;
+  const bool live = wid < p.n_rows;
+  const int w = live ? wid : p.n_rows - 1;                    // dead rows mirror the last row, store nothing
+  const int slot = w / p.num_q_heads, head = w - slot * p.num_q_heads;
   const int token = p.split_rows[2 * slot];
   const int ns = min(p.split_rows[2 * slot + 1], p.max_splits);
-  if (token < 0 || token >= p.total_q) return;
   const int64_t base = (int64_t(slot) * p.num_q_heads + head) * p.max_splits;
-  const float mk = lane < ns ? p.ml_part[(base + lane) * 2] : -INFINITY;
-  const float lk = lane < ns ? p.ml_part[(base + lane) * 2 + 1] : 0.f;
-  const float M = wave_max(mk);
+  const float mk = j < ns ? p.ml_part[(base + j) * 2] : -INFINITY;
+  const float lk = j < ns ? p.ml_part[(base + j) * 2 + 1] : 0.f;
+  // max and weighted sum over the row's lanes (xor shuffles stay inside the row)
+  float M = mk;
+#pragma unroll
+  for (int o = C::LANES / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   const float wk = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
-  float den = wave_sum(wk * lk);
-  constexpr int PER = D / 64;
-  float acc[PER];
+  float den = wk * lk;
 #pragma unroll
-  for (int x = 0; x < PER; ++x) acc[x] = 0.f;
-  const float* op = p.o_part + base * D + lane;
-#pragma unroll 8
-  for (int k = 0; k < ns; ++k) {
-    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k));  // split k's weight
+  for (int o = C::LANES / 2; o > 0; o >>= 1) den += __shfl_xor(den, o);
+  fvec acc = {};
+  const fvec* op = reinterpret_cast<const fvec*>(p.o_part + base * D) + j;
+  const int row0 = sub * C::LANES;   // first lane of this row
+  int k = 0;
+  for (; k + 4 <= ns; k += 4) {      // four splits' loads in flight
+    fvec v[4];
+    float wt[4];
 #pragma unroll
-    for (int x = 0; x < PER; ++x) acc[x] = fmaf(w, op[k * D + 64 * x], acc[x]);
+    for (int u = 0; u < 4; ++u) {
+      v[u] = op[(k + u) * C::LANES];
+      wt[u] = __shfl(wk, row0 + k + u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += wt[u] * v[u];
   }
+  for (; k < ns; ++k) acc += __shfl(wk, row0 + k) * op[k * C::LANES];
+  if (!live || token < 0 || token >= p.total_q) return;
   if (!(den > 0.f)) den = INFINITY;  // no visible key: output 0
-  const int64_t orow = (int64_t(token) * p.num_q_heads + head) * D;
+  const int64_t orow = (int64_t(token) * p.num_q_heads + head) * D + C::VEC * j;
 #pragma unroll
-  for (int x = 0; x < PER; ++x) {
+  for (int x = 0; x < C::VEC; ++x) {
     if (BF16)
-      static_cast<__bf16*>(p.out)[orow + lane + 64 * x] = (__bf16)(acc[x] / den);
+      static_cast<__bf16*>(p.out)[orow + x] = (__bf16)(acc[x] / den);
     else
-      static_cast<float*>(p.out)[orow + lane + 64 * x] = acc[x] / den;
+      static_cast<float*>(p.out)[orow + x] = acc[x] / den;
   }
 }
 
@@ -843,7 +856,9 @@ void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
     cp.n_rows = a.n_split_rows * a.shape.num_q_heads;
     cp.max_splits = a.max_splits;
     cp.total_q = a.total_q;
-    hipLaunchKernelGGL((combine_splits<D, BF16>), dim3((cp.n_rows + 3) / 4), dim3(256), 0, st, cp);
+    const int rows_per_block = 4 * CombineShape<D>::ROWS;
+    hipLaunchKernelGGL((combine_splits<D, BF16>), dim3((cp.n_rows + rows_per_block - 1) / rows_per_block), dim3(256),
+                       0, st, cp);
   }
 }
 
