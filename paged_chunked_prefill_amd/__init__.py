@@ -71,8 +71,11 @@ def _align256(x: int) -> int:
 
 
 # Work-list entry as laid out by the library (read back only by tests).
-WORK_ITEM_DTYPE = np.dtype([("req", "<i4"), ("kv_head", "<i4"), ("q_begin", "<i4"), ("q_count", "<i4"),
-                            ("kv_begin", "<i4"), ("kv_end", "<i4"), ("split", "<i4"), ("part_row", "<i4")])
+WORK_ITEM_DTYPE = np.dtype([("req", "<i4"), ("head_split", "<i4"), ("tok0", "<i4"), ("pos0", "<i4"),
+                            ("q_count", "<i4"), ("kv_begin", "<i4"), ("kv_end", "<i4"), ("part_row", "<i4")])
+SPLIT_BITS = 8
+# Decoded view: the packed fields plus KV head, split and the tile's first chunk token.
+WORK_ITEM_VIEW = np.dtype(WORK_ITEM_DTYPE.descr + [("kv_head", "<i4"), ("split", "<i4"), ("q_begin", "<i4")])
 
 
 def extend_metadata_size(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0):
@@ -121,6 +124,13 @@ class ExtendPlan:
             out[name] = raw[off:off + nbytes].view(dt).copy()
             off = _align256(off + nbytes)
         out["split_rows"] = out["split_rows"].reshape(-1, 2)
+        raw_items, items = out["items"], np.zeros(ni, WORK_ITEM_VIEW)
+        for f in WORK_ITEM_DTYPE.names:
+            items[f] = raw_items[f]
+        items["kv_head"] = raw_items["head_split"] >> SPLIT_BITS
+        items["split"] = raw_items["head_split"] & ((1 << SPLIT_BITS) - 1)
+        items["q_begin"] = raw_items["tok0"] - out["qo_indptr"][raw_items["req"]]
+        out["items"] = items
         return out
 
 

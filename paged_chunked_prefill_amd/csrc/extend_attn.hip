@@ -52,9 +52,6 @@ struct Params {
   const void* v_pool;
   const int32_t* page_table;
   const int32_t* req_pool_indices;
-  const int32_t* qo_indptr;
-  const int32_t* kv_indptr;
-  const int32_t* prefix_lens;
   const WorkItem* items;
   int32_t* status;
   void* out;
@@ -88,27 +85,24 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Per-item geometry shared by both instantiations.
 struct ItemView {
-  int req, kv_head, q_begin, q_count, kv_begin, kv_end, split, part_row;
-  int prefix, qo, pt_row;
+  int req, kv_head, split, q_count, kv_begin, kv_end, part_row;
+  int tok0, pos0, pt_row;
 };
 
 __device__ inline ItemView load_item(const Params& p) {
   const WorkItem it = p.items[blockIdx.x];
   ItemView v;
   v.req = it.req;
-  v.kv_head = it.kv_head;
-  v.q_begin = it.q_begin;
-  v.split = it.split;
+  v.kv_head = it.head_split >> kSplitBits;
+  v.split = it.head_split & ((1 << kSplitBits) - 1);
   v.part_row = it.part_row;
-  v.prefix = p.prefix_lens[it.req];
-  v.qo = p.qo_indptr[it.req];
-  const int chunk = p.qo_indptr[it.req + 1] - v.qo;
-  const int kv_len = p.kv_indptr[it.req + 1] - p.kv_indptr[it.req];
-  // never step outside the request, whatever the work item says
-  v.q_count = min(it.q_count, chunk - it.q_begin);
+  v.tok0 = it.tok0;
+  v.pos0 = it.pos0;
+  v.q_count = it.q_count;
   v.kv_begin = max(it.kv_begin, 0);
+  // never read past the page table's row, whatever the item says
   const int64_t addressable = int64_t(p.page_table_stride) * p.page_size;
-  v.kv_end = int(min(int64_t(min(it.kv_end, kv_len)), addressable));
+  v.kv_end = int(min(int64_t(it.kv_end), addressable));
   v.pt_row = p.req_pool_indices ? p.req_pool_indices[it.req] : it.req;
   return v;
 }
@@ -219,13 +213,13 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // this lane's query row: tile row r = token * G + head-in-group
   const int r = wave * 32 + l32;
   const int tok = r / G, gh = r - tok * G;
-  const int gtok = it.qo + it.q_begin + tok;                 // global token index
+  const int gtok = it.tok0 + tok;                            // global token index
   const bool row_live = tok < it.q_count && gtok < p.total_q;
-  const int qpos = it.prefix + it.q_begin + tok;             // absolute query position
+  const int qpos = it.pos0 + tok;                            // absolute query position
   const int head = it.kv_head * G + gh;
   const bool wave_live = wave * 32 < it.q_count * G;
-  const int qpos_first = it.prefix + it.q_begin;
-  const int qpos_last = it.prefix + it.q_begin + it.q_count - 1;
+  const int qpos_first = it.pos0;
+  const int qpos_last = it.pos0 + it.q_count - 1;
 
   f32x16 o[T::DBLK];
 #pragma unroll
@@ -368,33 +362,41 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     asm volatile("" ::: "memory");
   };
 
-  // prologue part 1: tiles 0..2 in flight
-  if (ntiles > 0) {
-    int ids[3][T::LOADS];
-#pragma unroll
-    for (int u = 0; u < 3; ++u) fetch_pages(ids[u], t0 + u * T::BC);
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      if (u < ntiles) {
-        prepare(ids[u], t0 + u * T::BC, stage_of(u), cp);
-#pragma unroll
-        for (int c2 = 0; c2 < 2 * T::LOADS; ++c2) issue(cp, c2);
-      }
-    }
-    newest_issued = ntiles > 2;
-  }
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7].
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7];
+  // loaded first, so that their latency overlaps the page-table reads below.
   // Rows past the tile read the tile's first token (finite, never stored), so
   // every lane loads and the loads are complete on every path after the wait
   // below: no later instruction ever has to wait for them (such a wait would
   // also wait for the gathers in flight).
   bf16x8 qf[T::KSTEPS];
   {
-    const int qtok = row_live ? gtok : it.qo + it.q_begin;
+    const int qtok = row_live ? gtok : it.tok0;
     const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
                                                        (int64_t(qtok) * p.num_q_heads + head) * D + 8 * half);
 #pragma unroll
     for (int ks = 0; ks < T::KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qrow[2 * ks]);
+  }
+  // prologue part 1: tiles 0..2 in flight. All three are gathered even when
+  // the item has fewer (clamped keys, see below), so that every page id is
+  // loaded up front with one wait.
+  if (ntiles > 0) {
+    int ids[3][T::LOADS];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) fetch_pages(ids[u], t0 + u * T::BC);
+    if constexpr (POW2_PAGES) {
+      // every id in hand here: the scalar loads go out together, one wait
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int i = 0; i < T::LOADS; ++i) asm volatile("" ::"s"(ids[u][i]));
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      prepare(ids[u], t0 + u * T::BC, stage_of(u), cp);
+#pragma unroll
+      for (int c2 = 0; c2 < 2 * T::LOADS; ++c2) issue(cp, c2);
+    }
+    newest_issued = true;
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // Q, tiles 0..2 landed
   asm volatile("" ::: "memory");
@@ -527,7 +529,6 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // Past the last tile the gathers still run, of keys clamped to the last one
   // (in bounds, mostly one repeated row) into stages that are no longer read,
   // which keeps the segment free of branches; they are waited for below.
-  newest_issued = true;
   for (int t = 0; t < ntiles; ++t) {
     const bool last = t + 1 >= ntiles;
     fetch_pages(pg, t0 + (t + 3) * T::BC);
@@ -609,9 +610,9 @@ __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
   const int G = p.group;
   const int r = wave * 32 + l32;
   const int tok = r / G, gh = r - tok * G;
-  const int gtok = it.qo + it.q_begin + tok;
+  const int gtok = it.tok0 + tok;
   const bool row_live = tok < it.q_count && gtok < p.total_q;
-  const int qpos = it.prefix + it.q_begin + tok;
+  const int qpos = it.pos0 + tok;
   const int head = it.kv_head * G + gh;
   const bool wave_live = wave * 32 < it.q_count * G;
 
@@ -871,9 +872,6 @@ int launch_extend_attn(const AttnArgs& a, void* stream) {
   p.v_pool = a.v_pool;
   p.page_table = a.page_table;
   p.req_pool_indices = a.req_pool_indices;
-  p.qo_indptr = a.qo_indptr;
-  p.kv_indptr = a.kv_indptr;
-  p.prefix_lens = a.prefix_lens;
   p.items = a.items;
   p.status = a.status;
   p.out = a.out;

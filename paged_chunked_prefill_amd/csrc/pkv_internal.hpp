@@ -37,17 +37,21 @@ constexpr int kXcds = 8;
 // One unit of attention work = one workgroup: a tile of consecutive chunk
 // tokens of one request, all G query heads of one KV head, over the key
 // positions [kv_begin, kv_end) (the whole visible range, or one split of it).
+// The planner resolves the request's offsets into the item, so a workgroup
+// starts from this one 32-byte record.
 struct alignas(16) WorkItem {
-  int32_t req;       // request index b
-  int32_t kv_head;   // KV head hk; query heads hk*G .. hk*G+G-1
-  int32_t q_begin;   // first chunk token of the tile (0-based within the chunk)
-  int32_t q_count;   // tokens in the tile (>= 1)
-  int32_t kv_begin;  // first key position this item covers
-  int32_t kv_end;    // one past the last key position (<= N_b)
-  int32_t split;     // split index within the tile's row (0 when unsplit)
-  int32_t part_row;  // -1: write `out`; else partial slot of the tile's first token
+  int32_t req;         // request index b (page-table row, or index into req_pool_indices)
+  int32_t head_split;  // KV head hk << 8 | split index within the tile's row (0 when unsplit)
+  int32_t tok0;        // global token index of the tile's first token: qo_indptr[b] + first chunk token
+  int32_t pos0;        // its absolute position: P_b + first chunk token
+  int32_t q_count;     // tokens in the tile (>= 1, all inside the chunk)
+  int32_t kv_begin;    // first key position this item covers
+  int32_t kv_end;      // one past the last key position (<= N_b)
+  int32_t part_row;    // -1: write `out`; else partial slot of the tile's first token
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
+constexpr int kSplitBits = 8;  // split index field of head_split (splits <= PKV_MAX_SPLITS < 256)
+static_assert(PKV_MAX_SPLITS < (1 << kSplitBits), "split index fits its field");
 
 // Byte offsets of the sections of the metadata buffer (host staging and its
 // device copy share the layout). Each section starts on a 256-byte boundary.

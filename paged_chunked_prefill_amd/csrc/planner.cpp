@@ -79,13 +79,10 @@ std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
     for (uint32_t i : ord) out.push_back(in[i]);
     return out;
   }
-  // locality groups: items with equal (request, KV head, split); the packed key
-  // is exact because KV heads < 2^24 (a token row is < 2^24 bytes) and splits <= 32
+  // locality groups: items with equal (request, KV head, split)
   std::vector<std::pair<uint64_t, uint32_t>> keyed(n);
   for (size_t i = 0; i < n; ++i)
-    keyed[i] = {(uint64_t(uint32_t(in[i].req)) << 32) | (uint64_t(uint32_t(in[i].kv_head)) << 8) |
-                    uint64_t(uint32_t(in[i].split) & 0xff),
-                uint32_t(i)};
+    keyed[i] = {(uint64_t(uint32_t(in[i].req)) << 32) | uint64_t(uint32_t(in[i].head_split)), uint32_t(i)};
   std::sort(keyed.begin(), keyed.end());
   std::vector<uint32_t> group_of(n);
   std::vector<int64_t> group_cost;
@@ -257,8 +254,9 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       for (int32_t k = 0; k < splits; ++k) {
         WorkItem it;
         it.req = t.req;
-        it.kv_head = h;
-        it.q_begin = t.q_begin;
+        it.head_split = (h << kSplitBits) | k;
+        it.tok0 = qo_start[t.req] + t.q_begin;
+        it.pos0 = prefix_lens[t.req] + t.q_begin;
         it.q_count = t.q_count;
         if (splits == 1) {
           it.kv_begin = t.kv_lo;
@@ -269,7 +267,6 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
           it.kv_begin = std::max(t.kv_lo, ga * kSplitGranule);
           it.kv_end = std::min(t.kv_hi, gb * kSplitGranule);
         }
-        it.split = k;
         it.part_row = part_row;
         items.push_back(it);
       }

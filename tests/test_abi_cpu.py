@@ -49,6 +49,12 @@ def test_indptrs_bit_exact():
     assert np.array_equal(h["prefix_lens"], w.prefix_lens)
     assert p.plan.total_q == 705 and p.plan.max_q_len == 512 and p.plan.max_kv_len == 1537
     assert h["status"][0] == 0
+    # every work item carries its tile's offsets (the attention reads nothing else to start)
+    it = h["items"]
+    r = it["req"]
+    assert np.array_equal(it["tok0"], qo[r] + it["q_begin"])
+    assert np.array_equal(it["pos0"], w.prefix_lens[r] + it["q_begin"])
+    assert np.all(it["q_begin"] + it["q_count"] <= w.chunk_lens[r]) and np.all(it["kv_end"] <= kv[r + 1] - kv[r])
     # bf16 items hold 256 query-head rows = 64 tokens x 4 heads: (1 + 1 + 2 + 8) tiles x 8 KV heads
     # = 96 < 256 resident slots, so the long tiles are split over KV
     tiles = {(int(i["req"]), int(i["kv_head"]), int(i["q_begin"])) for i in h["items"]}
