@@ -1,0 +1,82 @@
+"""Graph capture and replay of a step's path: append + extend attention (+ the
+split combine) captured once into a HIP graph, with the metadata built before
+capture and reused by every replay (the way a step's plan serves every layer).
+Each replay runs after eager work and a synchronization of its own and must
+reproduce the eager result exactly (same kernels, same inputs), which in turn
+meets the oracle bound. The library's launches record kernels only: no memset,
+allocation or synchronization is captured."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from pkv_testlib import assert_parity, oracle_out, oracle_pools
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_chunked_prefill_amd as pkv
+    from gpu_harness import DeviceCache, shape_of, upload_q, values_of
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    assert pkv.device_supported(torch.cuda.current_device()), "not a gfx950 device"
+
+
+def _workload(name):
+    if name == "ragged_splits":
+        return wl.config2()            # 96 tiles < 256 slots: long tiles are split, the combine runs
+    if name == "decode_splits":
+        w = wl.config5(decode_only=True)
+        return w.subset(list(range(8)))  # 8 one-token rows, 8 KV splits each
+    return wl.config4(mid_page=True)   # window, no splits
+
+
+@pytest.mark.parametrize("name", ["ragged_splits", "decode_splits", "window"])
+def test_graph_replay_matches_eager(name):
+    w = _workload(name)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    print(f"[graph] {name}: P={list(w.prefix_lens)[:4]} L={list(w.chunk_lens)[:4]} batch={w.batch}", flush=True)
+    cache = DeviceCache(w, dev)
+    cache.fill_prefix(w)
+    plan = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape_of(w), w.window, w.decode_splits, device=dev)
+    kn, vn = cache._gather_new_kv(w)
+    q = upload_q(w, dev)
+    out = torch.empty_like(q)
+    ws = plan.workspace()   # allocated before capture
+
+    def path():
+        pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan)
+        pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out, workspace=ws)
+
+    path()                  # eager: the reference result (appending again later writes the same bytes)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert pkv.read_status(plan) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path()              # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    scratch = torch.randn(1 << 20, device=dev)
+    for r in range(4):
+        out.fill_(float("nan"))                 # eager work between replays
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager result"
+    assert pkv.read_status(plan) == 0
+    if name == "ragged_splits":   # small enough for the whole oracle
+        ref = oracle_out(w, oracle_pools(w), dtype=np.float32)
+        rep = assert_parity(values_of(out), ref, w.dtype, f"graph {name}")
+        print(f"[parity] graph {name}: max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}", flush=True)
