@@ -9,13 +9,14 @@
 // reference for paged prefill).
 //
 // How (one workgroup per planner work item = GQA-packed query tile x key range):
-//  * The tile's rows are (token, query head) pairs of one KV head; four waves
-//    own 32 rows each, so the K/V tile staged in LDS serves all G heads.
-//  * Keys are walked in tiles aligned to absolute positions. Each key's page
-//    is looked up in the page table; its D-row is read from the pool with
-//    16-byte loads into registers (prefetching the next tile while the
-//    current one is computed) and then written to the other LDS stage.
-//    Positions outside the item's key range are zero-filled, never loaded.
+//  * The tile's rows are (token, query head) pairs of one KV head; eight waves
+//    own 32 rows each (256 rows), so every K/V tile staged in LDS serves all
+//    G heads of 256/G tokens.
+//  * Keys are walked in 64-key tiles aligned to absolute positions, through a
+//    4-stage LDS ring. A tile is gathered from the paged pool straight into
+//    LDS (global_load_lds, 16 bytes per lane, no register staging): the page
+//    id of each group of rows is a scalar load, and positions outside the
+//    item's key range read the nearest key inside it, which the mask removes.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K rows come from LDS, the wave's
 //    Q rows stay in registers. Each lane then holds 16 scores of one query row
 //    per 32-key block, so the row max needs one cross-half permlane swap and
@@ -25,9 +26,13 @@
 //    to bf16 in place (its register layout is already the B-operand layout);
 //    V^T fragments come from LDS through ds_read_b64_tr_b16, which transposes
 //    4x16-element blocks on the fly, so V needs no transposed copy.
+//  * Two groups of four waves (one wave of each on every SIMD) run the tile
+//    program one segment apart: one group's MFMA segment (PV of tile t, S of
+//    tile t+1) overlaps the other group's softmax segment.
 //  * Online softmax (running max and sum per row); split items store the
 //    unnormalised output with (max, sum) and a combine kernel merges splits.
-// The fp32 instantiation uses v_mfma_f32_32x32x2f32 with the same data flow.
+// fp32 inputs take a separate, simpler kernel (4 waves, 128 rows, 32-key tiles
+// staged through registers into a double-buffered LDS tile, v_mfma_f32_32x32x2f32).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -582,7 +587,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
 }
 
 // ---------------------------------------------------------------------------
-// fp32: 32-key tiles, 32x32x2 fp32 MFMA (same data flow, scalar operands)
+// fp32: 4 waves, 32-key tiles staged through registers, 32x32x2 fp32 MFMA
 // ---------------------------------------------------------------------------
 
 template <int D>
