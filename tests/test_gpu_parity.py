@@ -238,7 +238,8 @@ def test_split_zero_score_exact():
 
 @pytest.mark.parametrize("dtype,D,hq,hkv,ps,window", [
     ("bf16", 64, 4, 4, 1, 0), ("bf16", 128, 6, 2, 3, 0), ("bf16", 64, 12, 4, 7, 33), ("fp32", 128, 4, 1, 16, 0),
-    ("fp32", 64, 3, 3, 5, 10), ("bf16", 128, 16, 1, 64, 100)])
+    ("fp32", 64, 3, 3, 5, 10), ("bf16", 128, 16, 1, 64, 100), ("bf16", 128, 8, 8, 128, 0),
+    ("bf16", 128, 32, 2, 256, 57), ("bf16", 64, 128, 1, 16, 0), ("bf16", 128, 6, 3, 2, 0)])
 def test_variants(dtype, D, hq, hkv, ps, window):
     P = np.array([0, 37, 0, 130, 64], np.int32)
     L = np.array([70, 0, 1, 45, 129], np.int32)
@@ -247,6 +248,47 @@ def test_variants(dtype, D, hq, hkv, ps, window):
                     wl.shuffled_page_table(43, pages, P + L, ps))
     out, _, _ = prefill_and_attend(w)
     check(f"variant {dtype} D={D} {hq}/{hkv} ps={ps} W={window}", out, oracle_out(w, oracle_pools(w)), dtype)
+
+
+def test_one_row_longest_range_most_splits():
+    """One token after 131071 cached keys, split the most ways the ABI allows
+    (32), next to a short row: sampled against the oracle row by row."""
+    P = np.array([131071, 9], np.int32)
+    L = np.ones(2, np.int32)
+    pages = int(sum((int(n) + 15) // 16 for n in P + L))
+    w = wl.Workload("long1", 47, "bf16", 8, 2, 128, 16, pages, 0, P, L,
+                    wl.shuffled_page_table(47, pages, P + L, 16), decode_splits=pkv.PKV_MAX_SPLITS)
+    out, _, plan = prefill_and_attend(w)
+    assert plan.plan.max_splits == pkv.PKV_MAX_SPLITS
+    got = values_of(out)
+    for b in range(2):
+        check(f"long row N={int(P[b]) + 1} splits=32 req {b}", got[[b]], oracle_request_rows(w, b, [0]), "bf16")
+
+
+def test_window_with_split_tiles():
+    """A window and KV splits together (few long tiles: the planner cuts them)."""
+    P, L = np.array([3000], np.int32), np.array([300], np.int32)
+    pages = (3300 + 15) // 16
+    w = wl.Workload("wsplit", 48, "bf16", 16, 4, 128, 16, pages, 700, P, L,
+                    wl.shuffled_page_table(48, pages, P + L, 16))
+    out, _, plan = prefill_and_attend(w)
+    assert plan.plan.n_split_rows > 0
+    check("window 700 + splits", out, oracle_out(w, oracle_pools(w)), "bf16")
+
+
+def test_many_requests_more_items_than_slots():
+    """1000 one-token requests of assorted lengths: more work items than the
+    GPU has workgroup slots, each item's request resolved from its record."""
+    rng = np.random.default_rng(49)
+    P = rng.integers(0, 700, 1000).astype(np.int32)
+    L = np.ones(1000, np.int32)
+    pages = int(sum((int(n) + 15) // 16 for n in P + L))
+    w = wl.Workload("many", 49, "bf16", 8, 4, 64, 16, pages, 0, P, L, wl.shuffled_page_table(49, pages, P + L, 16))
+    out, _, plan = prefill_and_attend(w)
+    assert plan.plan.n_items > 256
+    got = values_of(out)
+    for b in (0, 1, 499, 998, 999):
+        check(f"many req {b}", got[[b]], oracle_request_rows(w, b, [0]), "bf16")
 
 
 def test_req_pool_indices_and_scale():
