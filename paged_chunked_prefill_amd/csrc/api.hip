@@ -203,10 +203,11 @@ int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, con
   a.status = plan->status;
   a.out = out;
   char* ws = static_cast<char*>(workspace);
-  a.o_part = plan->n_split_rows ? reinterpret_cast<float*>(ws) : nullptr;
+  a.o_part = plan->n_split_rows ? ws : nullptr;
   a.ml_part = plan->n_split_rows
                   ? reinterpret_cast<float*>(ws + workspace_o_bytes(plan->n_split_rows, shape->num_q_heads,
-                                                                    plan->max_splits, shape->head_dim))
+                                                                    plan->max_splits, shape->head_dim,
+                                                                    shape->dtype))
                   : nullptr;
   a.n_items = plan->n_items;
   a.n_split_rows = plan->n_split_rows;

@@ -60,7 +60,7 @@ struct Params {
   const WorkItem* items;
   int32_t* status;
   void* out;
-  float* o_part;
+  void* o_part;     // bf16 partials for the bf16 kernel, fp32 for the fp32 kernel
   float* ml_part;
   int32_t page_table_stride;
   int32_t num_q_heads;
@@ -571,13 +571,16 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   } else {
     const int64_t slot = int64_t(it.part_row + tok) * p.num_q_heads + head;
     const int64_t prow = slot * p.max_splits + it.split;
-    float* op = p.o_part + prow * D;
+    // unnormalised partial in bf16: one more rounding of the output's own size
+    uint16_t* op = static_cast<uint16_t*>(p.o_part) + prow * D;
 #pragma unroll
     for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
-        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * jj + 4 * half) = v;
+        bf16x4 v;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = (__bf16)o[db][4 * jj + x];
+        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj + 4 * half) = __builtin_bit_cast(u32x2, v);
       }
     if (half == 0) {
       p.ml_part[prow * 2] = m_ref;   // reference max (log2 units) the partial is relative to
@@ -744,7 +747,7 @@ __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
   } else {
     const int64_t slot = int64_t(it.part_row + tok) * p.num_q_heads + head;
     const int64_t prow = slot * p.max_splits + it.split;
-    float* op = p.o_part + prow * D;
+    float* op = static_cast<float*>(p.o_part) + prow * D;
 #pragma unroll
     for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
 // ---------------------------------------------------------------------------
 
 struct CombineParams {
-  const float* o_part;
+  const void* o_part;   // bf16 when BF16, else fp32
   const float* ml_part;
   const int32_t* split_rows;
   void* out;
@@ -810,7 +813,19 @@ __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
 #pragma unroll
   for (int o = C::LANES / 2; o > 0; o >>= 1) den += __shfl_xor(den, o);
   fvec acc = {};
-  const fvec* op = reinterpret_cast<const fvec*>(p.o_part + base * D) + j;
+  // lane j's VEC elements of split k's partial row
+  typedef uint16_t hvec __attribute__((ext_vector_type(C::VEC)));
+  auto part = [&](int k) __attribute__((always_inline)) {
+    if constexpr (BF16) {
+      const hvec h = reinterpret_cast<const hvec*>(static_cast<const uint16_t*>(p.o_part) + base * D)[k * C::LANES + j];
+      fvec v;
+#pragma unroll
+      for (int x = 0; x < C::VEC; ++x) v[x] = __uint_as_float(uint32_t(h[x]) << 16);
+      return v;
+    } else {
+      return reinterpret_cast<const fvec*>(static_cast<const float*>(p.o_part) + base * D)[k * C::LANES + j];
+    }
+  };
   const int row0 = sub * C::LANES;   // first lane of this row
   int k = 0;
   for (; k + 4 <= ns; k += 4) {      // four splits' loads in flight
@@ -818,13 +833,13 @@ __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
     float wt[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      v[u] = op[(k + u) * C::LANES];
+      v[u] = part(k + u);
       wt[u] = __shfl(wk, row0 + k + u);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc += wt[u] * v[u];
   }
-  for (; k < ns; ++k) acc += __shfl(wk, row0 + k) * op[k * C::LANES];
+  for (; k < ns; ++k) acc += __shfl(wk, row0 + k) * part(k);
   if (!live || token < 0 || token >= p.total_q) return;
   if (!(den > 0.f)) den = INFINITY;  // no visible key: output 0
   const int64_t orow = (int64_t(token) * p.num_q_heads + head) * D + C::VEC * j;

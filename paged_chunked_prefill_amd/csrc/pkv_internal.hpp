@@ -75,14 +75,17 @@ inline MetaLayout meta_layout(int32_t batch, int32_t n_items, int32_t n_split_ro
 }
 
 // Split partials in the workspace: for partial slot s, query head h, split k
-//   o_part [s][h][k][D] fp32 (unnormalised output)
+//   o_part [s][h][k][D] unnormalised output: bf16 for bf16 inputs (the output
+//                       precision; half the bytes the combine has to move),
+//                       fp32 for fp32 inputs
 //   ml_part[s][h][k][2] fp32 (running max in log2 units, running sum)
-inline size_t workspace_o_bytes(int32_t n_split_rows, int32_t hq, int32_t max_splits, int32_t d) {
-  return align256(sizeof(float) * size_t(n_split_rows) * hq * max_splits * d);
+inline size_t part_elem_bytes(int32_t dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 4; }
+inline size_t workspace_o_bytes(int32_t n_split_rows, int32_t hq, int32_t max_splits, int32_t d, int32_t dtype) {
+  return align256(part_elem_bytes(dtype) * size_t(n_split_rows) * hq * max_splits * d);
 }
-inline size_t workspace_bytes(int32_t n_split_rows, int32_t hq, int32_t max_splits, int32_t d) {
+inline size_t workspace_bytes(int32_t n_split_rows, int32_t hq, int32_t max_splits, int32_t d, int32_t dtype) {
   if (n_split_rows == 0) return 0;
-  return workspace_o_bytes(n_split_rows, hq, max_splits, d) +
+  return workspace_o_bytes(n_split_rows, hq, max_splits, d, dtype) +
          align256(sizeof(float) * size_t(n_split_rows) * hq * max_splits * 2);
 }
 
@@ -113,7 +116,7 @@ struct AttnArgs {
   const int32_t* split_rows;
   int32_t* status;
   void* out;
-  float* o_part;
+  void* o_part;   // bf16 or fp32 by dtype, see workspace_o_bytes
   float* ml_part;
   int32_t n_items;
   int32_t n_split_rows;

@@ -306,7 +306,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     plan->max_splits = max_splits;
     plan->window = window;
     plan->shape = *shape;
-    plan->workspace_bytes = workspace_bytes(n_split_rows, hq, max_splits, shape->head_dim);
+    plan->workspace_bytes = workspace_bytes(n_split_rows, hq, max_splits, shape->head_dim, shape->dtype);
   }
 
   if (meta_host) {

@@ -118,7 +118,8 @@ def test_config5_split_plan():
     p = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape(64, 8, 128, 16, w.num_pages), 0, 8)
     assert p.plan.n_items == 64 * 8 * 8 + 2 * 8 * (2048 // 32)      # 8 splits; 32-token tiles (G=8)
     assert p.plan.n_split_rows == 64 and p.plan.max_splits == 8
-    assert p.plan.workspace_bytes >= 64 * 64 * 8 * (128 + 2) * 4
+    # bf16 partial outputs (D x 2 bytes) plus fp32 (max, sum) per row, head and split
+    assert p.plan.workspace_bytes >= 64 * 64 * 8 * (128 * 2 + 2 * 4)
     mb, wb = pkv.extend_metadata_size(w.prefix_lens, w.chunk_lens, shape(64, 8, 128, 16, w.num_pages), 0, 8)
     assert wb == p.plan.workspace_bytes and mb == p.meta_host.size
 
