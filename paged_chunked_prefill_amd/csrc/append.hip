@@ -8,9 +8,10 @@
 // start_pos .. seq_len-1, and the backend writes k_buffer[out_cache_loc] = k.
 //
 // A token's K (or V) row of Hkv*D elements is contiguous both in k_new and in
-// its pool slot ([page][slot][Hkv][D]), so each thread moves one 16-byte
-// vector and a wave covers 1 KiB of consecutive source bytes: the copy is a
-// coalesced streaming scatter, bound by HBM bandwidth.
+// its pool slot ([page][slot][Hkv][D]). A workgroup owns one token (blockIdx.x)
+// and a span of its row's 16-byte vectors (blockIdx.y): the token's request,
+// position and page are uniform, so they come from scalar loads, and the row
+// loads are issued before the page lookup so that their latencies overlap.
 #include <hip/hip_runtime.h>
 
 #include "pkv_internal.hpp"
@@ -30,7 +31,6 @@ struct AppendParams {
   const int32_t* qo_indptr;
   const int32_t* prefix_lens;
   int32_t* status;
-  int64_t total_vecs;      // total_q * vecs_per_token
   int32_t vecs_per_token;  // Hkv * D * elem_bytes / 16
   int32_t batch;
   int32_t total_q;
@@ -39,9 +39,14 @@ struct AppendParams {
   int32_t num_pages;
 };
 
+// The index arrays are read-only here: reading them through the constant
+// address space lets the (uniform) lookups use scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ inline cint_ptr as_const(const int32_t* p) { return (cint_ptr)p; }
+
 // Request owning global token t: the last b with qo_indptr[b] <= t (requests
 // with an empty chunk share their qo_indptr value with the next request).
-__device__ inline int find_request(const int32_t* qo_indptr, int batch, int t) {
+__device__ inline int find_request(cint_ptr qo_indptr, int batch, int t) {
   int lo = 0, hi = batch;  // invariant: qo_indptr[lo] <= t < qo_indptr[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -51,28 +56,35 @@ __device__ inline int find_request(const int32_t* qo_indptr, int batch, int t) {
 }
 
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < p.total_vecs; i += stride) {
-    const int t = int(i / p.vecs_per_token);
-    const int v = int(i - int64_t(t) * p.vecs_per_token);
-    if (t >= p.total_q) break;
-    const int b = find_request(p.qo_indptr, p.batch, t);
-    const int pos = p.prefix_lens[b] + (t - p.qo_indptr[b]);
+  const int v = blockIdx.y * blockDim.x + threadIdx.x;   // vector within the token row
+  const bool lane_live = v < p.vecs_per_token;
+  for (int t = blockIdx.x; t < p.total_q; t += gridDim.x) {   // uniform per workgroup
+    const int64_t src = int64_t(t) * p.vecs_per_token + v;
+    u32x4 kv, vv;
+    if (lane_live) {
+      kv = p.k_new[src];
+      vv = p.v_new[src];
+    }
+    const int b = find_request(as_const(p.qo_indptr), p.batch, t);
+    const int pos = as_const(p.prefix_lens)[b] + (t - as_const(p.qo_indptr)[b]);
     const int col = pos / p.page_size;
-    if (pos < 0 || col >= p.page_table_stride) {
-      atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+    bool ok = pos >= 0 && col < p.page_table_stride;
+    int page = -1;
+    if (ok) {
+      const int row = p.req_pool_indices ? as_const(p.req_pool_indices)[b] : b;
+      page = as_const(p.page_table)[int64_t(row) * p.page_table_stride + col];
+      ok = page >= 0 && page < p.num_pages;
+    }
+    if (!ok) {
+      if (threadIdx.x == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
       continue;
     }
-    const int row = p.req_pool_indices ? p.req_pool_indices[b] : b;
-    const int page = p.page_table[int64_t(row) * p.page_table_stride + col];
-    if (page < 0 || page >= p.num_pages) {
-      atomicOr(p.status, PKV_STATUS_BAD_PAGE);
-      continue;
+    if (lane_live) {
+      const int64_t slot = int64_t(page) * p.page_size + (pos - col * p.page_size);
+      const int64_t dst = slot * p.vecs_per_token + v;
+      p.k_pool[dst] = kv;
+      p.v_pool[dst] = vv;
     }
-    const int64_t slot = int64_t(page) * p.page_size + (pos - col * p.page_size);
-    const int64_t dst = slot * p.vecs_per_token + v;
-    p.k_pool[dst] = p.k_new[i];
-    p.v_pool[dst] = p.v_new[i];
   }
 }
 
@@ -94,15 +106,16 @@ int launch_append(const AppendArgs& a, void* stream) {
   p.prefix_lens = a.prefix_lens;
   p.status = a.status;
   p.vecs_per_token = int32_t(row_bytes / 16);
-  p.total_vecs = int64_t(a.total_q) * p.vecs_per_token;
   p.batch = a.batch;
   p.total_q = a.total_q;
   p.page_size = a.shape.page_size;
   p.page_table_stride = a.page_table_stride;
   p.num_pages = a.shape.num_pages;
-  const int64_t want = (p.total_vecs + 255) / 256;
-  const int blocks = int(want < 65536 ? want : 65536);
-  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  // x: tokens (one workgroup each, looping past 2^20); y: spans of a row's vectors
+  const int threads = p.vecs_per_token >= 256 ? 256 : ((p.vecs_per_token + 63) / 64) * 64;
+  const int spans = (p.vecs_per_token + threads - 1) / threads;
+  const int blocks = a.total_q < (1 << 20) ? a.total_q : (1 << 20);
+  hipLaunchKernelGGL(append_kernel, dim3(blocks, spans), dim3(threads), 0, static_cast<hipStream_t>(stream), p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(PKV_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
