@@ -171,6 +171,14 @@ struct Bf16Tile {
   static constexpr int LOADS = BC / RPI / NW;    // such copies per wave per tensor and tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
+  // The item's Q rows are gathered into LDS once, over the ring's last stage
+  // (first written by the gather of tile 3, after the prologue) and the space
+  // after the ring, then read into registers.
+  static constexpr int QBYTES = 32 * NW * ROWB;             // 32 rows per wave
+  static constexpr int QOFF = (NSTAGE - 1) * STAGE;
+  static constexpr int LDS_BYTES = QOFF + QBYTES;
+  static constexpr int QCOPIES = QBYTES / 1024 / NW;        // wave-wide 1 KiB copies per wave
+  static_assert(QBYTES >= STAGE, "the Q region covers the last stage");
   // XOR swizzles of the 16-byte chunks of a row (64 banks of 4 bytes = 256 B
   // per bank row; a D=64 row is half of one). K: the 16 lanes of a b128 read
   // that issue together read 16 rows at one chunk index; chunk c of row r sits
@@ -205,7 +213,7 @@ __device__ __forceinline__ void pin_m_schedule() {
 template <int D, bool POW2_PAGES>
 __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
   const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char*)smem));
 
   const ItemView it = load_item(p);
@@ -367,23 +375,23 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     asm volatile("" ::: "memory");
   };
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7];
-  // loaded first, so that their latency overlaps the page-table reads below.
-  // Rows past the tile read the tile's first token (finite, never stored), so
-  // every lane loads and the loads are complete on every path after the wait
-  // below: no later instruction ever has to wait for them (such a wait would
-  // also wait for the gathers in flight).
-  bf16x8 qf[T::KSTEPS];
-  {
-    const int qtok = row_live ? gtok : it.tok0;
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
-                                                       (int64_t(qtok) * p.num_q_heads + head) * D + 8 * half);
+  // prologue part 1: the item's Q rows gathered into LDS like the K rows (same
+  // copy shape and swizzle; rows past the item read the item's first token:
+  // finite, never stored), issued first.
 #pragma unroll
-    for (int ks = 0; ks < T::KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qrow[2 * ks]);
+  for (int c = 0; c < T::QCOPIES; ++c) {
+    const int r = T::RPI * (T::NW * c + wave) + lrow;   // tile row = token * G + head-in-group
+    int qt = r / G;
+    const int qh = r - qt * G;
+    if (qt >= it.q_count || it.tok0 + qt >= p.total_q) qt = 0;
+    const char* src = static_cast<const char*>(p.q) +
+                      ((int64_t(it.tok0 + qt) * p.num_q_heads + it.kv_head * G + qh) * D) * 2 +
+                      16 * ((lane % T::CH) ^ T::kswz(r));
+    lds_copy16(src, lds0 + T::QOFF + T::RPI * (T::NW * c + wave) * T::ROWB);
   }
-  // prologue part 1: tiles 0..2 in flight. All three are gathered even when
-  // the item has fewer (clamped keys, see below), so that every page id is
-  // loaded up front with one wait.
+  // tiles 0..2 in flight. All three are gathered even when the item has fewer
+  // (clamped keys, see below), so that every page id is loaded up front with
+  // one wait.
   if (ntiles > 0) {
     int ids[3][T::LOADS];
 #pragma unroll
@@ -403,10 +411,21 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     }
     newest_issued = true;
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // Q, tiles 0..2 landed
+  // Q and tile 0 landed; tiles 1 and 2 may still be in flight (the loop's
+  // waits cover them). Without POW2_PAGES the page ids are vector loads the
+  // compiler waits for with everything older: wait for all here.
+  if (POW2_PAGES && ntiles > 0)
+    __builtin_amdgcn_s_waitcnt(kWaitVm<4 * T::LOADS>);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7]
+  bf16x8 qf[T::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < T::KSTEPS; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(smem + T::QOFF + wave * 32 * T::ROWB + koff[ks]);
 
   f32x16 s[2];            // scores S^T of the tile in flight (two 32-key blocks)
   bf16x8 pb[2][2];        // P of the tile being accumulated, as B operands
