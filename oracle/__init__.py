@@ -13,6 +13,14 @@ Parity status of each function (what pins it is listed in the tests):
                     torch scaled_dot_product_attention on the full sequence
                     (causal, GQA, band mask), W=1 and single-key identities,
                     bitwise partition invariance
+  rope_rows         pinned: identity, quarter and half turns (exact), the
+                    hand-worked adjacent-pair example, complex multiplication,
+                    norm preservation, angle composition and the relative-
+                    position identity of the dot product; the bf16 rounding
+                    agrees with float32 round-to-nearest-even references
+  rope_append       pinned: V copied bit for bit, K equal to rope_rows at the
+                    absolute position, chunk-by-chunk equal to one full call
 """
 from .paged_attention import (append_kv, extend_attention, extend_metadata, gather_kv,  # noqa: F401
                                visible_range)
+from .rope import positions_of, rope_append, rope_rows, rotate_pairs, round_to_bf16_bits  # noqa: F401

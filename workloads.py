@@ -234,6 +234,15 @@ class Workload:
                                    page_table=self.page_table[reqs].copy(), request_ids=ids)
 
 
+def rope_table(table_len: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """Rotary-embedding table: (cos, sin) of p * base**(-2j/D) for positions
+    p < table_len and pairs j, float32 [table_len, D/2, 2] (the pages' freqs_cis
+    layout, one row per position). An input: the method takes any table."""
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    ang = np.arange(table_len, dtype=np.float64)[:, None] * base ** (-2.0 * j / head_dim)[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
 def shuffled_page_table(config_id: int, num_pages: int, kv_lens: Sequence[int], page_size: int,
                         stride: Optional[int] = None, pad: int = -1) -> np.ndarray:
     """Request b gets the next ceil(N_b/ps) ids of a seeded permutation of the pool;
