@@ -101,6 +101,9 @@ def main():
                     help="also time the step replayed from captured HIP graphs (append + attention per batch, "
                          "metadata built once), reported as graph_replay")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows for the CPU oracle sample (0: auto)")
+    ap.add_argument("--rope", action="store_true",
+                    help="the step rotates q and k at their absolute positions with pkv_rope_append (in place "
+                         "of pkv_append) before the attention; reports that kernel's HBM rate")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -142,6 +145,11 @@ def main():
         cache.fill_prefix(w)
     nsteps = args.warmup + args.steps
 
+    # rotary table (cos, sin) of every position the workload reaches, for --rope
+    import workloads as wl
+    max_pos = max(int((np.asarray(bw.prefix_lens) + np.asarray(bw.chunk_lens)).max()) for bw in batches)
+    rope_table = torch.from_numpy(wl.rope_table(max_pos + 1, w.head_dim)).to(dev) if args.rope else None
+    esize = 2 if w.dtype == "bf16" else 4
     # per batch: device inputs, output, metadata buffers, pre-marshalled ctypes arguments
     B = []
     for bw in batches:
@@ -164,9 +172,23 @@ def main():
         b["meta_args"] = [(len(L), P.ctypes.data_as(ctypes.c_void_p), L.ctypes.data_as(ctypes.c_void_p),
                            ctypes.byref(shape), bw.window, splits, vp(h), meta_bytes, vp(meta_dev), meta_bytes,
                            ctypes.byref(plan), sh) for h in hosts]
-        b["append_args"] = (vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
-                            cache.page_table.shape[1], None, ctypes.byref(plan), ctypes.byref(shape), sh)
-        b["attn_args"] = (vp(q), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table), cache.page_table.shape[1],
+        if args.rope:
+            # q is rotated into q_rot, which the attention reads; per token the kernel moves q, K and V
+            # in and out once and reads one table row
+            b["q_rot"] = torch.empty_like(q)
+            b["append_fn"] = lib.pkv_rope_append
+            b["append_args"] = (vp(q), vp(b["q_rot"]), vp(kn), vp(vn), vp(rope_table), rope_table.shape[0],
+                                vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table), cache.page_table.shape[1],
+                                None, ctypes.byref(plan), ctypes.byref(shape), sh)
+            b["append_bytes"] = int(L.sum()) * (2 * esize * w.head_dim * (w.num_q_heads + 2 * w.num_kv_heads) +
+                                                4 * w.head_dim)
+        else:
+            b["append_fn"] = lib.pkv_append
+            b["append_args"] = (vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
+                                cache.page_table.shape[1], None, ctypes.byref(plan), ctypes.byref(shape), sh)
+            b["append_bytes"] = int(L.sum()) * 4 * esize * w.head_dim * w.num_kv_heads
+        q_attn = b["q_rot"] if args.rope else q
+        b["attn_args"] = (vp(q_attn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table), cache.page_table.shape[1],
                           None, None, None, None, bw.window, 0.0, ctypes.byref(plan), ctypes.byref(shape), vp(out),
                           vp(ws), ws.numel(), sh)
         B.append(b)
@@ -175,13 +197,13 @@ def main():
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in B]
           for _ in range(nsteps)]
-    build, append, attn = lib.build_extend_metadata, lib.pkv_append, lib.paged_extend_attn
+    build, attn = lib.build_extend_metadata, lib.paged_extend_attn
 
     def step(s):
         for i, b in enumerate(B):
             if build(*b["meta_args"][s]):
                 raise RuntimeError(lib.pkv_last_error().decode())
-            if append(*b["append_args"]):
+            if b["append_fn"](*b["append_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
             ev[s][i][0].record(stream)
             if attn(*b["attn_args"]):
@@ -200,6 +222,18 @@ def main():
 
     attn_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.warmup, nsteps)) / args.steps
                for i in range(len(B))]
+    # the appends (or rotary appends) of a step, timed in a pass of their own after the timed steps so that
+    # their events do not add to the step (rewriting the same slots and q rows: idempotent)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        for b in B:
+            if b["append_fn"](*b["append_args"]):
+                raise RuntimeError(lib.pkv_last_error().decode())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_ms = e0.elapsed_time(e1) / args.steps
+    append_bytes = sum(b["append_bytes"] for b in B)
     flops = sum(b["flops"] for b in B)
     hbm_bytes = sum(b["bytes"] for b in B)
     tokens = sum(b["total_q"] for b in B)
@@ -247,7 +281,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
-        "config": {"workload": desc, "name": args.workload, "batches_per_step": len(B),
+        "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope), "batches_per_step": len(B),
                    "query_tokens_per_step": tokens, "flops_per_step": flops},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
@@ -256,6 +290,10 @@ def main():
                       "hbm_gbs_algorithmic": round(attn_gbs, 1), "per_launch_ms": [round(x, 4) for x in attn_ms]},
         "roofline": roofline, "cpu_baseline": cpu, "setup_s": round(setup_s, 2),
     }
+    line["append"] = {"kernel": "pkv_rope_append (rotary q, k + append)" if args.rope else "pkv_append",
+                      "ms_per_step": round(append_ms, 4), "bytes_per_step": append_bytes,
+                      "gbs_algorithmic": round(append_bytes / (append_ms * 1e-3) / 1e9, 1) if append_ms > 0 else None,
+                      "hbm_frac": round(append_bytes / (append_ms * 1e-3) / 1e9 / HBM_PEAK, 4) if append_ms > 0 else None}
     if graph_replay is not None:
         line["graph_replay"] = graph_replay
     print(json.dumps(line), flush=True)
@@ -276,12 +314,12 @@ def time_graph_replay(args, B, lib, flops, tokens):
         at = b["attn_args"][:-1] + (sh,)
         torch.cuda.synchronize()
         with torch.cuda.stream(s):       # one eager pass on the capture stream first
-            if lib.pkv_append(*ap) or lib.paged_extend_attn(*at):
+            if b["append_fn"](*ap) or lib.paged_extend_attn(*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            if lib.pkv_append(*ap) or lib.paged_extend_attn(*at):
+            if b["append_fn"](*ap) or lib.paged_extend_attn(*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
         graphs.append(g)
     for _ in range(args.warmup):

@@ -163,6 +163,38 @@ int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                const pkv_shape* shape, pkv_stream_t stream);
 
 /*
+ * pkv_rope_append -- rotary position embedding of the chunk's new query and
+ * key rows fused with the KV append (AstrAI compare v1.3.12..925cbed,
+ * csrc/kernels/rotary_emb.cu: bf16 rows rotated with an fp32 (cos, sin)
+ * table of [.., head_dim/2, 2]; the CUDA backend's prefill path then writes
+ * the step's K/V into the cache slots; AReno PR #642: a later chunk's rows sit
+ * at absolute positions behind the cached prefix).
+ *
+ * For token i of request b at absolute position p = P_b + i, pair j of every
+ * head row (elements 2j, 2j+1) is rotated by row p of the table:
+ *   (a, b) -> (a*cos - b*sin, a*sin + b*cos),  (cos, sin) = rope_table[p][j]
+ * in fp32 and rounded once to the storage type (round to nearest even):
+ *   q_out[t][h]                  rotated q[t][h] for every query head h
+ *   k_pool slot of position p    rotated k_new[t][h] for every KV head h
+ *   v_pool slot of position p    v_new[t][h], a bit copy
+ * The slot of p is (page_table[row_b][p / page_size], p % page_size), as in
+ * pkv_append; no other pool byte is written. Rotating every chunk at its
+ * absolute positions makes a chunked prefill equal to one full prefill.
+ *   q, q_out       [total_q, Hq, D]; q_out may equal q (in place), else the
+ *                  two must not overlap; neither may overlap the pools
+ *   rope_table     device fp32 [rope_table_len][D/2][2], 16-byte aligned
+ *   rope_table_len positions the table holds; must be >= plan->max_kv_len
+ * Errors: PKV_ERR_INVALID_ARGUMENT (null pointer, misaligned or too short
+ * table, plan/shape mismatch, page-table stride too small),
+ * PKV_ERR_UNSUPPORTED, PKV_ERR_HIP. A page id outside the pool sets
+ * PKV_STATUS_BAD_PAGE and that token is skipped.
+ */
+int pkv_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, const float* rope_table,
+                    int32_t rope_table_len, void* k_pool, void* v_pool, const int32_t* page_table,
+                    int32_t page_table_stride, const int32_t* req_pool_indices, const pkv_plan* plan,
+                    const pkv_shape* shape, pkv_stream_t stream);
+
+/*
  * paged_extend_attn -- steps a3..a9: attention of every chunk row over its
  * request's prefix plus chunk (AReno PR #642; AstrAI compare,
  * attn_paged_test.cu CPU reference for paged prefill: query head h reads KV

@@ -7,6 +7,7 @@ stream. The functions carry the C names:
 
   build_extend_metadata(prefix_lens, chunk_lens, shape, window, decode_splits, device)
   pkv_append(k_new, v_new, k_pool, v_pool, page_table, plan)
+  pkv_rope_append(q, k_new, v_new, rope_table, k_pool, v_pool, page_table, plan)
   paged_extend_attn(q, k_pool, v_pool, page_table, plan, out=None, ...)
 
 There is no fallback: if libpkv.so is missing, importing this package
@@ -223,6 +224,40 @@ def pkv_append(k_new, v_new, k_pool, v_pool, page_table, plan: ExtendPlan, req_p
                            ctypes.c_void_p(req_pool_indices.data_ptr()) if req_pool_indices is not None else None,
                            ctypes.byref(plan.plan), ctypes.byref(s), _stream_handle(stream, k_pool.device)),
            "pkv_append")
+
+
+def pkv_rope_append(q, k_new, v_new, rope_table, k_pool, v_pool, page_table, plan: ExtendPlan, q_out=None,
+                    req_pool_indices=None, stream=None):
+    """Rotate the chunk's q and k rows at their absolute positions with
+    ``rope_table`` (float32 [table_len, D/2, 2] = cos, sin) and write rotated K
+    and V into their page slots. Returns q_out (a new tensor unless given;
+    pass q itself to rotate in place)."""
+    import torch
+    s = plan.shape
+    dt = _torch_dtype(s.dtype)
+    tq = plan.plan.total_q
+    _expect(q, (tq, s.num_q_heads, s.head_dim), dt, "q")
+    _expect(k_new, (tq, s.num_kv_heads, s.head_dim), dt, "k_new")
+    _expect(v_new, (tq, s.num_kv_heads, s.head_dim), dt, "v_new")
+    _expect(k_pool, _pool_shape(s), dt, "k_pool")
+    _expect(v_pool, _pool_shape(s), dt, "v_pool")
+    if rope_table.dtype != torch.float32 or rope_table.dim() != 3 or tuple(rope_table.shape[1:]) != (s.head_dim // 2, 2) \
+            or not rope_table.is_contiguous() or rope_table.device != q.device:
+        raise ValueError(f"rope_table: expected contiguous float32 [n, {s.head_dim // 2}, 2] on {q.device}, got "
+                         f"{rope_table.dtype} {tuple(rope_table.shape)} on {rope_table.device}")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _expect(q_out, (tq, s.num_q_heads, s.head_dim), dt, "q_out")
+    _check_tables(page_table, plan, req_pool_indices)
+    _check(_lib.pkv_rope_append(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(q_out.data_ptr()),
+                                ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+                                ctypes.c_void_p(rope_table.data_ptr()), rope_table.shape[0],
+                                ctypes.c_void_p(k_pool.data_ptr()), ctypes.c_void_p(v_pool.data_ptr()),
+                                ctypes.c_void_p(page_table.data_ptr()), page_table.shape[1],
+                                ctypes.c_void_p(req_pool_indices.data_ptr()) if req_pool_indices is not None else None,
+                                ctypes.byref(plan.plan), ctypes.byref(s), _stream_handle(stream, k_pool.device)),
+           "pkv_rope_append")
+    return q_out
 
 
 def paged_extend_attn(q, k_pool, v_pool, page_table, plan: ExtendPlan, out=None, window: Optional[int] = None,

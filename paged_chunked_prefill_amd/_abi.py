@@ -14,8 +14,8 @@ PKV_DTYPE_FP32 = 1
 PKV_STATUS_BAD_PAGE = 1
 PKV_MAX_SPLITS = 32
 
-EXPORTS = ("pkv_extend_metadata_size", "build_extend_metadata", "pkv_append", "paged_extend_attn",
-           "pkv_read_status", "pkv_last_error", "pkv_device_supported")
+EXPORTS = ("pkv_extend_metadata_size", "build_extend_metadata", "pkv_append", "pkv_rope_append",
+           "paged_extend_attn", "pkv_read_status", "pkv_last_error", "pkv_device_supported")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
@@ -59,6 +59,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "build_extend_metadata": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _P, _SZ, _P, _SZ,
                                   ctypes.POINTER(PkvPlan), _P],
         "pkv_append": [_P, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P],
+        "pkv_rope_append": [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PkvPlan),
+                            ctypes.POINTER(PkvShape), _P],
         "paged_extend_attn": [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, ctypes.c_float,
                               ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P, _SZ, _P],
         "pkv_read_status": [ctypes.POINTER(PkvPlan), ctypes.POINTER(_I32), _P],

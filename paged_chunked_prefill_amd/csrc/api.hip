@@ -162,6 +162,44 @@ int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
   return launch_append(a, stream);
 }
 
+int pkv_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, const float* rope_table,
+                    int32_t rope_table_len, void* k_pool, void* v_pool, const int32_t* page_table,
+                    int32_t page_table_stride, const int32_t* req_pool_indices, const pkv_plan* plan,
+                    const pkv_shape* shape, pkv_stream_t stream) {
+  g_error[0] = 0;
+  int st = check_plan(plan, shape, "pkv_rope_append");
+  if (st) return st;
+  if ((st = check_page_table(page_table, page_table_stride, plan, "pkv_rope_append"))) return st;
+  if (plan->total_q > 0 && (!q || !q_out || !k_new || !v_new || !k_pool || !v_pool || !rope_table))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_rope_append: q, q_out, K/V, pools and rope_table must not be NULL");
+  if (rope_table && (reinterpret_cast<uintptr_t>(rope_table) & 15))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_rope_append: rope_table must be 16-byte aligned");
+  if (plan->total_q > 0 && rope_table_len < plan->max_kv_len)
+    return set_error(PKV_ERR_INVALID_ARGUMENT,
+                     "pkv_rope_append: rope_table has %d positions, the batch reaches position %d", rope_table_len,
+                     plan->max_kv_len - 1);
+  if ((st = check_current_device())) return st;
+  AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.page_table_stride = page_table_stride;
+  a.req_pool_indices = req_pool_indices;
+  a.qo_indptr = plan->qo_indptr;
+  a.prefix_lens = plan->prefix_lens;
+  a.status = plan->status;
+  a.batch = plan->batch;
+  a.total_q = plan->total_q;
+  a.shape = *shape;
+  a.q = q;
+  a.q_out = q_out;
+  a.rope_table = rope_table;   // non-NULL whenever there are rows (checked above)
+  a.rope_table_len = rope_table_len;
+  return launch_append(a, stream);
+}
+
 int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
                       int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
                       const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,

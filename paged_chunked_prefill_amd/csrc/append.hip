@@ -88,6 +88,101 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   }
 }
 
+// Rotary embedding of the token's query and key rows, fused with the append
+// (AstrAI compare v1.3.12..925cbed, csrc/kernels/rotary_emb.cu: an fp32 table
+// of (cos, sin) per pair of head dimensions, [.., head_dim/2, 2]; the backend's
+// prefill path then writes K/V into the cache slots). Pair j of a head row is
+// elements 2j and 2j+1: (a, b) -> (a cos - b sin, a sin + b cos), in fp32,
+// rounded once to the storage type; the table row is the token's absolute
+// position P_b + i. A workgroup owns one token; its lanes take the 16-byte
+// vectors of the token's Q row, K row and V row in turn (V is copied as is).
+struct RopeParams {
+  AppendParams ap;
+  const u32x4* q;
+  u32x4* q_out;
+  const float* table;
+  int32_t table_len;
+  int32_t head_dim;
+  int32_t q_vecs;   // 16-byte vectors of a token's Q row (Hq * D * elem / 16)
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(1024) void rope_append_kernel(const RopeParams r) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const AppendParams& p = r.ap;
+  constexpr int EPV = BF16 ? 8 : 4;   // elements per 16-byte vector
+  const int kv_vecs = p.vecs_per_token;
+  const int v = blockIdx.y * blockDim.x + threadIdx.x;   // slot: Q vectors, then K, then V
+  const bool lane_live = v < r.q_vecs + 2 * kv_vecs;
+  for (int t = blockIdx.x; t < p.total_q; t += gridDim.x) {   // uniform per workgroup
+    const int b = find_request(as_const(p.qo_indptr), p.batch, t);
+    const int pos = as_const(p.prefix_lens)[b] + (t - as_const(p.qo_indptr)[b]);
+    const int col = pos / p.page_size;
+    bool ok = pos >= 0 && col < p.page_table_stride && pos < r.table_len;
+    int page = -1;
+    if (ok) {
+      const int row = p.req_pool_indices ? as_const(p.req_pool_indices)[b] : b;
+      page = as_const(p.page_table)[int64_t(row) * p.page_table_stride + col];
+      ok = page >= 0 && page < p.num_pages;
+    }
+    if (!ok) {
+      if (threadIdx.x == 0 && blockIdx.y == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
+      continue;
+    }
+    if (!lane_live) continue;
+    const bool is_q = v < r.q_vecs, is_v = v >= r.q_vecs + kv_vecs;
+    const int vec = is_q ? v : (is_v ? v - r.q_vecs - kv_vecs : v - r.q_vecs);
+    const int64_t slot = int64_t(page) * p.page_size + (pos - col * p.page_size);
+    if (is_v) {
+      p.v_pool[slot * kv_vecs + vec] = p.v_new[int64_t(t) * kv_vecs + vec];
+      continue;
+    }
+    const u32x4 raw = is_q ? r.q[int64_t(t) * r.q_vecs + vec] : p.k_new[int64_t(t) * kv_vecs + vec];
+    // this vector's first pair within its head row, and the table row of the position
+    const int pair0 = ((vec * EPV) % r.head_dim) / 2;
+    const float* cs = r.table + (int64_t(pos) * (r.head_dim / 2) + pair0) * 2;
+    float x[EPV], c[EPV];
+    if constexpr (BF16) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = float(h[e]);
+      const f32x8 tv = *reinterpret_cast<const f32x8*>(cs);   // 4 pairs' (cos, sin), 32-byte aligned
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = tv[e];
+    } else {
+      const f32x4 h = __builtin_bit_cast(f32x4, raw);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = h[e];
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(cs);   // 2 pairs' (cos, sin)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = tv[e];
+    }
+    float y[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV / 2; ++k) {
+      const float a = x[2 * k], bb = x[2 * k + 1], co = c[2 * k], si = c[2 * k + 1];
+      y[2 * k] = a * co - bb * si;
+      y[2 * k + 1] = a * si + bb * co;
+    }
+    u32x4 res;
+    if constexpr (BF16) {
+      bf16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = (__bf16)y[e];
+      res = __builtin_bit_cast(u32x4, h);
+    } else {
+      const f32x4 h = {y[0], y[1], y[2], y[3]};
+      res = __builtin_bit_cast(u32x4, h);
+    }
+    if (is_q)
+      r.q_out[int64_t(t) * r.q_vecs + vec] = res;
+    else
+      p.k_pool[slot * kv_vecs + vec] = res;
+  }
+}
+
 }  // namespace
 
 int launch_append(const AppendArgs& a, void* stream) {
@@ -111,11 +206,32 @@ int launch_append(const AppendArgs& a, void* stream) {
   p.page_size = a.shape.page_size;
   p.page_table_stride = a.page_table_stride;
   p.num_pages = a.shape.num_pages;
-  // x: tokens (one workgroup each, looping past 2^20); y: spans of a row's vectors
-  const int threads = p.vecs_per_token >= 256 ? 256 : ((p.vecs_per_token + 63) / 64) * 64;
-  const int spans = (p.vecs_per_token + threads - 1) / threads;
   const int blocks = a.total_q < (1 << 20) ? a.total_q : (1 << 20);
-  hipLaunchKernelGGL(append_kernel, dim3(blocks, spans), dim3(threads), 0, static_cast<hipStream_t>(stream), p);
+  if (a.rope_table) {
+    // x: tokens; y: spans of the token's Q, K and V vectors (up to 1024 lanes each)
+    RopeParams r;
+    r.ap = p;
+    r.q = static_cast<const u32x4*>(a.q);
+    r.q_out = static_cast<u32x4*>(a.q_out);
+    r.table = a.rope_table;
+    r.table_len = a.rope_table_len;
+    r.head_dim = a.shape.head_dim;
+    r.q_vecs = int32_t(int64_t(a.shape.num_q_heads) * a.shape.head_dim * esize / 16);
+    const int total = r.q_vecs + 2 * p.vecs_per_token;
+    const int threads = total >= 1024 ? 1024 : ((total + 63) / 64) * 64;
+    const int spans = (total + threads - 1) / threads;
+    if (a.shape.dtype == PKV_DTYPE_BF16)
+      hipLaunchKernelGGL(rope_append_kernel<true>, dim3(blocks, spans), dim3(threads), 0,
+                         static_cast<hipStream_t>(stream), r);
+    else
+      hipLaunchKernelGGL(rope_append_kernel<false>, dim3(blocks, spans), dim3(threads), 0,
+                         static_cast<hipStream_t>(stream), r);
+  } else {
+    // x: tokens (one workgroup each, looping past 2^20); y: spans of a row's vectors
+    const int threads = p.vecs_per_token >= 256 ? 256 : ((p.vecs_per_token + 63) / 64) * 64;
+    const int spans = (p.vecs_per_token + threads - 1) / threads;
+    hipLaunchKernelGGL(append_kernel, dim3(blocks, spans), dim3(threads), 0, static_cast<hipStream_t>(stream), p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(PKV_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   return PKV_OK;

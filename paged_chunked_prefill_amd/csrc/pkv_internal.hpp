@@ -143,6 +143,11 @@ struct AppendArgs {
   int32_t batch;
   int32_t total_q;
   pkv_shape shape;
+  // rotary embedding fused with the append (rope_table == nullptr: plain append)
+  const void* q = nullptr;
+  void* q_out = nullptr;
+  const float* rope_table = nullptr;   // [rope_table_len][D/2][2] (cos, sin)
+  int32_t rope_table_len = 0;
 };
 
 int launch_append(const AppendArgs& a, void* stream);
