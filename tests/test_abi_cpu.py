@@ -199,6 +199,10 @@ def test_host_only_plan_cannot_launch():
                                ctypes.byref(s), dummy, None, 0, None)
     assert st == pkv.PKV_ERR_INVALID_ARGUMENT
     assert "device metadata" in lib.pkv_last_error().decode()
+    st = lib.pkv_rope_append(dummy, dummy, dummy, dummy, dummy, 64, dummy, dummy, dummy, 4, None,
+                             ctypes.byref(p.plan), ctypes.byref(s), None)
+    assert st == pkv.PKV_ERR_INVALID_ARGUMENT
+    assert "device metadata" in lib.pkv_last_error().decode()
 
 
 def test_auto_splits_follow_the_cu_heuristic():
