@@ -290,10 +290,15 @@ def main():
                       "hbm_gbs_algorithmic": round(attn_gbs, 1), "per_launch_ms": [round(x, 4) for x in attn_ms]},
         "roofline": roofline, "cpu_baseline": cpu, "setup_s": round(setup_s, 2),
     }
+    rope_cpu = None
+    if args.rope and not args.no_cpu_baseline:
+        rope_cpu = cpu_rope_baseline(batches, w, rope_table.cpu().numpy())
     line["append"] = {"kernel": "pkv_rope_append (rotary q, k + append)" if args.rope else "pkv_append",
                       "ms_per_step": round(append_ms, 4), "bytes_per_step": append_bytes,
                       "gbs_algorithmic": round(append_bytes / (append_ms * 1e-3) / 1e9, 1) if append_ms > 0 else None,
                       "hbm_frac": round(append_bytes / (append_ms * 1e-3) / 1e9 / HBM_PEAK, 4) if append_ms > 0 else None}
+    if rope_cpu is not None:
+        line["append"]["cpu_baseline"] = rope_cpu
     if graph_replay is not None:
         line["graph_replay"] = graph_replay
     print(json.dumps(line), flush=True)
@@ -412,6 +417,38 @@ def copy_calibration(args):
     torch.cuda.synchronize()
     print(json.dumps({"workload": "copy_calibration", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                       "launches": args.warmup + args.steps}), flush=True)
+
+
+def cpu_rope_baseline(batches, w, table_np):
+    """The CPU oracle's rotary append (oracle/rope.py, as it is) on the step's
+    first batch: q and k rows rotated at their positions and written with v
+    into the slots of a compact pool; GB/s on the kernel's algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    bw = batches[0]
+    P, L = np.asarray(bw.prefix_lens, np.int64), np.asarray(bw.chunk_lens, np.int64)
+    tq = int(L.sum())
+    rng = np.random.default_rng(0)
+    mk = lambda *s: wl.to_storage(rng.standard_normal(s).astype(np.float32), w.dtype)  # noqa: E731
+    q, k, v = mk(tq, w.num_q_heads, w.head_dim), mk(tq, w.num_kv_heads, w.head_dim), mk(tq, w.num_kv_heads, w.head_dim)
+    ps = w.page_size
+    npg = [int((p + l + ps - 1) // ps) for p, l in zip(P, L)]
+    pt = np.full((len(L), max(npg)), 0, np.int32)
+    off = 0
+    for b, c in enumerate(npg):
+        pt[b, :c] = np.arange(off, off + c)
+        off += c
+    pool = np.zeros((off, ps, w.num_kv_heads, w.head_dim), wl.storage_np_dtype(w.dtype))
+    t0 = time.perf_counter()
+    oracle.rope_append(q, k, v, table_np, pool, pool.copy(), pt, P, L, w.dtype)
+    dt = time.perf_counter() - t0
+    esize = 2 if w.dtype == "bf16" else 4
+    nbytes = tq * (2 * esize * w.head_dim * (w.num_q_heads + 2 * w.num_kv_heads) + 4 * w.head_dim)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3), "sample": f"the step's first batch ({tq} tokens), fp64 NumPy rotary oracle"}
 
 
 def cpu_baseline(w, batches, sample_rows):
