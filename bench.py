@@ -51,6 +51,15 @@ def workload(name):
         desc = (f"{n}-token prompt prefilled in {len(chunks)} chunks of <= {b} tokens; 16 query / 4 KV heads, "
                 f"head_dim 128, page_size 64, bf16")
         return w, wl.chunked_steps(w, chunks), False, desc
+    if name.startswith("budget"):
+        # budgetB_decodeN: the 4097-token prompt in chunks of B - N tokens, each step also N decode rows
+        bb, nd = name[len("budget"):].split("_decode")
+        w, steps = wl.budget_steps(4097, int(bb), int(nd))
+        desc = (f"4097-token prompt prefilled under a {bb}-token step budget shared with {nd} decoding requests "
+                f"(cached 1024..8192): {len(steps)} steps of {nd} one-token rows + a {int(bb) - int(nd)}-token "
+                f"chunk; 16 query / 4 KV heads, head_dim 128, page_size 64, bf16")
+        # the decode rows' cached prefixes are written first (up to their last step's position)
+        return w, steps, True, desc
     if name == "ragged4":
         w = wl.config2()
         return w, [w], True, "ragged batch P={0,100,513,1025} L={1,64,128,512}; 32/8 heads, D=128, ps=16, bf16"

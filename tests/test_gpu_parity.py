@@ -212,6 +212,21 @@ def test_config5_mixed_full_size():
         check(f"config5 prefill req {b}", got[[base + r for r in rows]], oracle_request_rows(w, b, rows), "bf16")
 
 
+def test_budget_steps_decode_rows_and_chunks():
+    """A prompt prefilled under a step budget shared with ongoing decodes: every
+    step's one-token rows and prompt chunk against the oracle at that step's
+    lengths (the pools hold all positions; each row reads only its visible ones)."""
+    w, steps = wl.budget_steps(prompt=700, budget=160, n_decode=8)
+    pools = oracle_pools(w)
+    cache = DeviceCache(w)
+    cache.fill_prefix(w)
+    for s_, st in enumerate(steps):
+        out, plan = run_attention(cache, st, decode_splits=0)
+        ref = oracle_out(st, pools)
+        check(f"budget step {s_} ({int(st.chunk_lens[-1])}-token chunk at {int(st.prefix_lens[-1])})",
+              out, ref, "bf16")
+
+
 @pytest.mark.parametrize("splits", [1, 3, 8, 0])
 def test_decode_splits_agree(splits):
     w = wl.config5(decode_only=True).subset(range(6))

@@ -321,6 +321,37 @@ def chunked_steps(w: Workload, chunks: Sequence[int]) -> List[Workload]:
     return steps
 
 
+def budget_steps(prompt: int = 4097, budget: int = 512, n_decode: int = 32,
+                 config_id: int = 6) -> Tuple[Workload, List[Workload]]:
+    """Chunked prefill under a per-step token budget shared with ongoing decodes
+    (AReno PR #642, "Performance": an ongoing request keeps decoding while an
+    incoming prompt is prefilled in budget-sized chunks). Every step holds the
+    n_decode one-token rows (cached lengths uniform in 1024..8192, one more per
+    step) first, then the prompt's next chunk of budget - n_decode tokens.
+    16 query / 4 KV heads, D=128, 64-token pages, bf16. Returns the workload at
+    its final lengths (its page table covers every step) and the steps."""
+    chunk = budget - n_decode
+    if chunk < 1:
+        raise ValueError("budget must leave room for the prompt")
+    chunks = chunk_partition(prompt, chunk)
+    n_steps = len(chunks)
+    dec0 = rng(config_id, LEN_STREAM).integers(1024, 8192, size=n_decode, endpoint=True).astype(np.int32)
+    P_fin = np.concatenate([dec0 + n_steps - 1, [0]]).astype(np.int32)
+    L_fin = np.concatenate([np.ones(n_decode, np.int32), [prompt]]).astype(np.int32)
+    ps = 64
+    need = int(sum((int(n) + ps - 1) // ps for n in P_fin + L_fin))
+    pt = shuffled_page_table(config_id, need + 8, P_fin + L_fin, ps)
+    w = Workload(f"budget{budget}_decode{n_decode}", config_id, "bf16", 16, 4, 128, ps, need + 8, 0,
+                 P_fin, L_fin, pt)
+    steps, p = [], 0
+    for s_, c in enumerate(chunks):
+        P = np.concatenate([dec0 + s_, [p]]).astype(np.int32)
+        L = np.concatenate([np.ones(n_decode, np.int32), [c]]).astype(np.int32)
+        steps.append(w.with_lengths(P, L, f"{w.name}/step{s_}"))
+        p += c
+    return w, steps
+
+
 def config4(mid_page: bool = False) -> Workload:
     """8 requests, 6000 cached + 1000 new, window 4096, Hq=32, Hkv=8, D=128, ps=16.
     ``mid_page`` uses prefixes 6001+2b so every append starts inside a page."""
