@@ -67,6 +67,13 @@ enum { PKV_DTYPE_BF16 = 0, PKV_DTYPE_FP32 = 1 };
 
 enum { PKV_STATUS_BAD_PAGE = 1 };
 
+/* Flags of build_extend_metadata_ex. PKV_FLAG_NON_CAUSAL: every row of a
+ * request sees all N_b of its keys, chunk rows after it included (AstrAI
+ * compare v1.3.12..925cbed, attn_paged_prefill: is_causal=False gives a
+ * causal offset of -1, no causal mask; attn_paged_test.cu tests it with
+ * q_len = kv_len). Incompatible with a sliding window. */
+enum { PKV_FLAG_NON_CAUSAL = 1 };
+
 /* Largest number of KV splits of one tile of query rows. */
 #define PKV_MAX_SPLITS 32
 
@@ -92,6 +99,7 @@ typedef struct pkv_plan {
   int32_t n_split_rows;   /* query tokens computed as KV splits + combine       */
   int32_t max_splits;     /* split stride of the partial buffers                */
   int32_t window;         /* sliding window W (<= 0: none)                      */
+  int32_t flags;          /* PKV_FLAG_* the plan was built with                 */
   pkv_shape shape;        /* the shape the plan was built for                   */
   size_t workspace_bytes; /* scratch paged_extend_attn needs (0 if no splits)   */
   /* device pointers (NULL after a host-only build) */
@@ -143,6 +151,22 @@ int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int
                           const pkv_shape* shape, int32_t window, int32_t decode_splits,
                           void* meta_host, size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes,
                           pkv_plan* plan_out, pkv_stream_t stream);
+
+/*
+ * build_extend_metadata_ex, pkv_extend_metadata_size_ex -- the same with
+ * `flags` (PKV_FLAG_*; 0 is build_extend_metadata). With PKV_FLAG_NON_CAUSAL
+ * each tile's key range is its request's whole [0, N_b) and the attention
+ * applies no causal bound; pkv_append and paged_extend_attn take the plan
+ * unchanged. Errors as build_extend_metadata, plus PKV_ERR_INVALID_ARGUMENT
+ * for unknown flags or a window with PKV_FLAG_NON_CAUSAL.
+ */
+int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                             const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
+                             void* meta_host, size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes,
+                             pkv_plan* plan_out, pkv_stream_t stream);
+int pkv_extend_metadata_size_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                                const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
+                                size_t* meta_bytes, size_t* workspace_bytes);
 
 /*
  * pkv_append -- step a2: write the chunk's new K/V into the pools

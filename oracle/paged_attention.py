@@ -112,13 +112,15 @@ def visible_range(pos: int, window: int) -> Tuple[int, int]:
 def extend_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, page_table: np.ndarray,
                      prefix_lens: Sequence[int], chunk_lens: Sequence[int], window: int = 0,
                      sm_scale: Optional[float] = None, req_pool_indices: Optional[np.ndarray] = None,
-                     dtype=np.float32, rows: Optional[Iterable[int]] = None) -> np.ndarray:
+                     dtype=np.float32, rows: Optional[Iterable[int]] = None, causal: bool = True) -> np.ndarray:
     """Attention output [total_q, Hq, D] for a ragged batch of chunks.
 
     ``q`` holds the chunk queries [total_q, Hq, D] in request order; the pools
     already contain every request's prefix and chunk K/V. ``rows`` restricts the
     work to those global token indices (other rows are left NaN), for sampled
-    checks of large batches."""
+    checks of large batches. ``causal=False`` (AstrAI compare,
+    attn_paged_prefill with is_causal=False: no causal offset) lets every row
+    see all N_b keys of its request, chunk rows after it included."""
     q = np.asarray(q)
     total_q, hq, d = q.shape
     hkv = k_pool.shape[2]
@@ -147,7 +149,7 @@ def extend_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, page
             t = int(qo[b]) + i
             if want is not None and t not in want:
                 continue
-            lo, hi = visible_range(P + i, window)
+            lo, hi = visible_range(P + i, window) if causal else (0, n)
             if hi <= lo:
                 continue                                    # no visible key -> 0
             for kvh in range(hkv):

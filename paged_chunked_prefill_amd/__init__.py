@@ -22,6 +22,7 @@ import numpy as np
 
 from . import _abi
 from ._abi import (PKV_DTYPE_BF16, PKV_DTYPE_FP32, PKV_ERR_HIP, PKV_ERR_INVALID_ARGUMENT,  # noqa: F401
+                   PKV_FLAG_NON_CAUSAL,
                    PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_MAX_SPLITS, PKV_OK, PKV_STATUS_BAD_PAGE,
                    PkvPlan, PkvShape)
 
@@ -79,12 +80,18 @@ SPLIT_BITS = 8
 WORK_ITEM_VIEW = np.dtype(WORK_ITEM_DTYPE.descr + [("kv_head", "<i4"), ("split", "<i4"), ("q_begin", "<i4")])
 
 
-def extend_metadata_size(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0):
+def extend_metadata_size(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0,
+                         causal: bool = True):
     P, L = _i32(prefix_lens), _i32(chunk_lens)
     mb, wb = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(_lib.pkv_extend_metadata_size(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                         int(decode_splits), ctypes.byref(mb), ctypes.byref(wb)),
-           "pkv_extend_metadata_size")
+    if causal:
+        _check(_lib.pkv_extend_metadata_size(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
+                                             int(decode_splits), ctypes.byref(mb), ctypes.byref(wb)),
+               "pkv_extend_metadata_size")
+    else:
+        _check(_lib.pkv_extend_metadata_size_ex(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
+                                                PKV_FLAG_NON_CAUSAL, int(decode_splits), ctypes.byref(mb),
+                                                ctypes.byref(wb)), "pkv_extend_metadata_size_ex")
     return mb.value, wb.value
 
 
@@ -143,35 +150,41 @@ def _stream_handle(stream, device):
 
 
 def build_extend_metadata(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0,
-                          device=None, stream=None, meta_host=None, meta_dev=None) -> ExtendPlan:
+                          device=None, stream=None, meta_host=None, meta_dev=None, causal: bool = True) -> ExtendPlan:
     """Plan one step. ``device=None`` plans on the host only (no GPU call).
     ``meta_host`` (pinned uint8 tensor) and ``meta_dev`` (device uint8 tensor)
     may be given to reuse buffers; the host one must not be rewritten before
-    the copy enqueued here has run."""
+    the copy enqueued here has run. ``causal=False`` plans with
+    PKV_FLAG_NON_CAUSAL (build_extend_metadata_ex): every row sees its whole
+    request."""
     P, L = _i32(prefix_lens), _i32(chunk_lens)
     plan = PkvPlan()
+
+    def call(host_ptr, host_bytes, dev_ptr, dev_bytes, st):
+        if causal:
+            return _check(_lib.build_extend_metadata(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
+                                                     int(decode_splits), host_ptr, host_bytes, dev_ptr, dev_bytes,
+                                                     ctypes.byref(plan), st), "build_extend_metadata")
+        return _check(_lib.build_extend_metadata_ex(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
+                                                    PKV_FLAG_NON_CAUSAL, int(decode_splits), host_ptr, host_bytes,
+                                                    dev_ptr, dev_bytes, ctypes.byref(plan), st),
+                      "build_extend_metadata_ex")
+
     if meta_host is not None and meta_dev is not None:
-        _check(_lib.build_extend_metadata(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                          int(decode_splits), ctypes.c_void_p(meta_host.data_ptr()),
-                                          meta_host.numel(), ctypes.c_void_p(meta_dev.data_ptr()),
-                                          meta_dev.numel(), ctypes.byref(plan),
-                                          _stream_handle(stream, meta_dev.device)), "build_extend_metadata")
+        call(ctypes.c_void_p(meta_host.data_ptr()), meta_host.numel(), ctypes.c_void_p(meta_dev.data_ptr()),
+             meta_dev.numel(), _stream_handle(stream, meta_dev.device))
         return ExtendPlan(plan, shape, meta_host, meta_dev, P, L)
-    meta_bytes, _ = extend_metadata_size(P, L, shape, window, decode_splits)
+    meta_bytes, _ = extend_metadata_size(P, L, shape, window, decode_splits, causal)
     if device is None:
         host = np.zeros(meta_bytes, np.uint8)
-        _check(_lib.build_extend_metadata(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                          int(decode_splits), _ptr(host), meta_bytes, None, 0,
-                                          ctypes.byref(plan), None), "build_extend_metadata")
+        call(_ptr(host), meta_bytes, None, 0, None)
         return ExtendPlan(plan, shape, host, None, P, L)
     import torch
     device = torch.device(device)
     host = torch.empty(meta_bytes, dtype=torch.uint8, pin_memory=True)
     dev = torch.empty(meta_bytes, dtype=torch.uint8, device=device)
-    _check(_lib.build_extend_metadata(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                      int(decode_splits), ctypes.c_void_p(host.data_ptr()), meta_bytes,
-                                      ctypes.c_void_p(dev.data_ptr()), meta_bytes, ctypes.byref(plan),
-                                      _stream_handle(stream, device)), "build_extend_metadata")
+    call(ctypes.c_void_p(host.data_ptr()), meta_bytes, ctypes.c_void_p(dev.data_ptr()), meta_bytes,
+         _stream_handle(stream, device))
     return ExtendPlan(plan, shape, host, dev, P, L)
 
 

@@ -12,9 +12,11 @@ PKV_ERR_HIP = -4
 PKV_DTYPE_BF16 = 0
 PKV_DTYPE_FP32 = 1
 PKV_STATUS_BAD_PAGE = 1
+PKV_FLAG_NON_CAUSAL = 1
 PKV_MAX_SPLITS = 32
 
-EXPORTS = ("pkv_extend_metadata_size", "build_extend_metadata", "pkv_append", "pkv_rope_append",
+EXPORTS = ("pkv_extend_metadata_size", "build_extend_metadata", "pkv_extend_metadata_size_ex",
+           "build_extend_metadata_ex", "pkv_append", "pkv_rope_append",
            "paged_extend_attn", "pkv_read_status", "pkv_last_error", "pkv_device_supported")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -29,7 +31,8 @@ class PkvShape(ctypes.Structure):
 class PkvPlan(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("total_q", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
                 ("max_kv_len", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_split_rows", ctypes.c_int32),
-                ("max_splits", ctypes.c_int32), ("window", ctypes.c_int32), ("shape", PkvShape),
+                ("max_splits", ctypes.c_int32), ("window", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("shape", PkvShape),
                 ("workspace_bytes", ctypes.c_size_t),
                 ("qo_indptr", ctypes.c_void_p), ("kv_indptr", ctypes.c_void_p),
                 ("prefix_lens", ctypes.c_void_p), ("items", ctypes.c_void_p),
@@ -58,6 +61,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
         "build_extend_metadata": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _P, _SZ, _P, _SZ,
                                   ctypes.POINTER(PkvPlan), _P],
+        "pkv_extend_metadata_size_ex": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _I32,
+                                        ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
+        "build_extend_metadata_ex": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _I32, _P, _SZ, _P, _SZ,
+                                     ctypes.POINTER(PkvPlan), _P],
         "pkv_append": [_P, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P],
         "pkv_rope_append": [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PkvPlan),
                             ctypes.POINTER(PkvShape), _P],

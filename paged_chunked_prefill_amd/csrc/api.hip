@@ -89,30 +89,45 @@ int pkv_device_supported(int device) {
   return ok;
 }
 
-int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
-                             const pkv_shape* shape, int32_t window, int32_t decode_splits, size_t* meta_bytes,
-                             size_t* workspace_bytes_out) {
+int pkv_extend_metadata_size_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                                const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
+                                size_t* meta_bytes, size_t* workspace_bytes_out) {
   g_error[0] = 0;
   if (!meta_bytes || !workspace_bytes_out)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_extend_metadata_size: output pointers must not be NULL");
   pkv_plan plan;
-  const int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, decode_splits, 0, nullptr, 0,
-                             &plan, meta_bytes);
+  const int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, flags, decode_splits, 0, nullptr,
+                             0, &plan, meta_bytes);
   if (st) return st;
   *workspace_bytes_out = plan.workspace_bytes;
   return PKV_OK;
+}
+
+int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                             const pkv_shape* shape, int32_t window, int32_t decode_splits, size_t* meta_bytes,
+                             size_t* workspace_bytes_out) {
+  return pkv_extend_metadata_size_ex(batch, prefix_lens_h, chunk_lens_h, shape, window, 0, decode_splits,
+                                     meta_bytes, workspace_bytes_out);
 }
 
 int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                           const pkv_shape* shape, int32_t window, int32_t decode_splits, void* meta_host,
                           size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes, pkv_plan* plan_out,
                           pkv_stream_t stream) {
+  return build_extend_metadata_ex(batch, prefix_lens_h, chunk_lens_h, shape, window, 0, decode_splits, meta_host,
+                                  meta_host_bytes, meta_dev, meta_dev_bytes, plan_out, stream);
+}
+
+int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
+                             const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
+                             void* meta_host, size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes,
+                             pkv_plan* plan_out, pkv_stream_t stream) {
   g_error[0] = 0;
   if (!meta_host || !plan_out)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "build_extend_metadata: meta_host and plan_out must not be NULL");
   size_t total = 0;
   pkv_plan plan;
-  int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, decode_splits, 0, meta_host,
+  int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, flags, decode_splits, 0, meta_host,
                        meta_host_bytes, &plan, &total);
   if (st) return st;
   if (meta_dev) {

@@ -50,7 +50,10 @@ struct alignas(16) WorkItem {
   int32_t part_row;    // -1: write `out`; else partial slot of the tile's first token
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
-constexpr int kSplitBits = 8;  // split index field of head_split (splits <= PKV_MAX_SPLITS < 256)
+constexpr int kSplitBits = 8;
+// Non-causal plans put an item's pos0 (the position its causal bound is taken
+// from) past every key, so the kernels' causal test passes for all of them.
+constexpr int32_t kNonCausalPos = 1 << 30;  // split index field of head_split (splits <= PKV_MAX_SPLITS < 256)
 static_assert(PKV_MAX_SPLITS < (1 << kSplitBits), "split index fits its field");
 
 // Byte offsets of the sections of the metadata buffer (host staging and its
@@ -92,8 +95,8 @@ inline size_t workspace_bytes(int32_t n_split_rows, int32_t hq, int32_t max_spli
 // Host planner (planner.cpp). Fills `meta_host` (may be NULL for a size query)
 // and the host fields of `plan`. Returns a PKV status; sets the error text.
 int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_lens, const pkv_shape* shape,
-                int32_t window, int32_t decode_splits, int32_t num_cus, void* meta_host, size_t meta_host_bytes,
-                pkv_plan* plan, size_t* meta_bytes_out);
+                int32_t window, int32_t flags, int32_t decode_splits, int32_t num_cus, void* meta_host,
+                size_t meta_host_bytes, pkv_plan* plan, size_t* meta_bytes_out);
 
 int validate_shape(const pkv_shape* shape);
 

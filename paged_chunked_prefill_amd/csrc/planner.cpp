@@ -128,14 +128,19 @@ std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
 }  // namespace
 
 int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_lens, const pkv_shape* shape,
-                int32_t window, int32_t decode_splits, int32_t num_cus, void* meta_host, size_t meta_host_bytes,
-                pkv_plan* plan, size_t* meta_bytes_out) {
+                int32_t window, int32_t flags, int32_t decode_splits, int32_t num_cus, void* meta_host,
+                size_t meta_host_bytes, pkv_plan* plan, size_t* meta_bytes_out) {
   if (int st = validate_shape(shape)) return st;
   if (batch < 1) return set_error(PKV_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
   if (!prefix_lens || !chunk_lens) return set_error(PKV_ERR_INVALID_ARGUMENT, "length arrays must not be NULL");
   if (decode_splits < 0 || decode_splits > PKV_MAX_SPLITS)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "decode_splits must be in 0..%d (got %d)", PKV_MAX_SPLITS,
                      decode_splits);
+  if (flags & ~PKV_FLAG_NON_CAUSAL)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", unsigned(flags));
+  const bool causal = !(flags & PKV_FLAG_NON_CAUSAL);
+  if (!causal && window > 0)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "a sliding window (%d) needs the causal mask", window);
   if (num_cus < 1) num_cus = kNominalCUs;
 
   const int32_t hq = shape->num_q_heads, hkv = shape->num_kv_heads;
@@ -174,7 +179,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       t.q_count = std::min(tile_tokens, L - q0);
       // the tile's first row sees keys from max(0, P+q0-W+1); its last row up to P+q0+count-1
       t.kv_lo = window > 0 ? int32_t(std::max<int64_t>(0, int64_t(P) + q0 - window + 1)) : 0;
-      t.kv_hi = P + q0 + t.q_count;
+      t.kv_hi = causal ? P + q0 + t.q_count : P + L;   // non-causal: every row sees the whole request
       t.one_token = (L == 1);
       tiles.push_back(t);
     }
@@ -256,7 +261,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
         it.req = t.req;
         it.head_split = (h << kSplitBits) | k;
         it.tok0 = qo_start[t.req] + t.q_begin;
-        it.pos0 = prefix_lens[t.req] + t.q_begin;
+        it.pos0 = causal ? prefix_lens[t.req] + t.q_begin : kNonCausalPos;
         it.q_count = t.q_count;
         if (splits == 1) {
           it.kv_begin = t.kv_lo;
@@ -305,6 +310,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     plan->n_split_rows = n_split_rows;
     plan->max_splits = max_splits;
     plan->window = window;
+    plan->flags = flags;
     plan->shape = *shape;
     plan->workspace_bytes = workspace_bytes(n_split_rows, hq, max_splits, shape->head_dim, shape->dtype);
   }

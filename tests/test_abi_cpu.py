@@ -30,10 +30,28 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
-def test_struct_sizes_match_header_layout():
-    # pkv_shape: 6 int32; pkv_plan: 8 int32 + shape + size_t + 6 pointers
-    assert ctypes.sizeof(pkv.PkvShape) == 24
-    assert ctypes.sizeof(pkv.PkvPlan) == 8 * 4 + 24 + 8 + 6 * 8
+def test_struct_sizes_match_header_layout(tmp_path):
+    """The ctypes mirrors against the header itself: a C program built with
+    gcc from include/pkv.h prints every field's offset and each struct's size."""
+    import subprocess
+    structs = {"pkv_shape": pkv.PkvShape, "pkv_plan": pkv.PkvPlan}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "pkv.h"', 'int main(void) {']
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True, text=True)
+               .stdout.splitlines())
+    for cname, cls in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(cls, fname).offset, f"{cname}.{fname}"
 
 
 def shape(hq=32, hkv=8, d=128, ps=16, pages=4096, dtype="bf16"):
@@ -228,3 +246,42 @@ def test_prefill_tiles_split_only_when_few():
             assert it["kv_end"] - it["kv_begin"] >= 64
     many = pkv.build_extend_metadata([16384, 16384], [2048, 2048], shape(64, 8, 128, 16, 5000))
     assert many.plan.n_items == 2 * 8 * 64 and many.plan.n_split_rows == 0
+
+
+def test_non_causal_plan_covers_whole_requests():
+    """PKV_FLAG_NON_CAUSAL: every tile's key range, merged over its splits, is its
+    request's whole [0, N_b); pos0 sits past every key."""
+    s = shape()
+    P, L = [0, 37, 500, 3000], [256, 64, 1, 300]
+    p = pkv.build_extend_metadata(P, L, s, causal=False)
+    assert p.plan.flags == pkv.PKV_FLAG_NON_CAUSAL
+    it = p.host_sections()["items"]
+    assert (it["pos0"] == 1 << 30).all()
+    ranges = {}
+    for x in it:
+        ranges.setdefault((int(x["req"]), int(x["q_begin"]), int(x["kv_head"])), []).append(
+            (int(x["kv_begin"]), int(x["kv_end"])))
+    for (b, _, _), rs in ranges.items():
+        rs.sort()
+        assert rs[0][0] == 0 and rs[-1][1] == P[b] + L[b]
+        assert all(a[1] == c[0] for a, c in zip(rs, rs[1:])), rs
+    # the causal plan of the same batch bounds each tile by its last row
+    pc = pkv.build_extend_metadata(P, L, s)
+    assert pc.plan.flags == 0
+    assert max(int(x["kv_end"]) for x in pc.host_sections()["items"] if x["req"] == 0 and x["q_begin"] == 0) == 64
+
+
+def test_non_causal_flag_errors():
+    lib = pkv.lib()
+    s = shape()
+    P, L = np.array([3], np.int32), np.array([2], np.int32)
+    mb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 0, 2, 0, ctypes.byref(mb),
+                                           ctypes.byref(wb)) == pkv.PKV_ERR_INVALID_ARGUMENT
+    assert "flags" in lib.pkv_last_error().decode()
+    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 5, pkv.PKV_FLAG_NON_CAUSAL, 0,
+                                           ctypes.byref(mb), ctypes.byref(wb)) == pkv.PKV_ERR_INVALID_ARGUMENT
+    assert "window" in lib.pkv_last_error().decode()
+    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 0, pkv.PKV_FLAG_NON_CAUSAL, 0,
+                                           ctypes.byref(mb), ctypes.byref(wb)) == pkv.PKV_OK

@@ -227,6 +227,27 @@ def test_budget_steps_decode_rows_and_chunks():
               out, ref, "bf16")
 
 
+@pytest.mark.parametrize("dtype,P,L,hq,hkv,D", [
+    ("bf16", [0, 0], [256, 128], 32, 4, 128),          # the pages' non-causal case: q_len = kv_len
+    ("bf16", [100, 37, 0], [64, 200, 1], 16, 4, 128),  # extend: rows also see the chunk rows after them
+    ("bf16", [0], [300], 8, 8, 64),
+    ("fp32", [20, 0], [45, 33], 4, 2, 64)])
+def test_non_causal(dtype, P, L, hq, hkv, D):
+    P, L = np.array(P, np.int32), np.array(L, np.int32)
+    ps = 16
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 4
+    pt = wl.shuffled_page_table(7, pages, P + L, ps)
+    w = wl.Workload("noncausal", 7, dtype, hq, hkv, D, ps, pages, 0, P, L, pt)
+    cache = DeviceCache(w)
+    cache.fill_prefix(w)
+    plan = pkv.build_extend_metadata(P, L, shape_of(w), 0, 0, device="cuda", causal=False)
+    kn, vn = cache._gather_new_kv(w)
+    pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan)
+    out = pkv.paged_extend_attn(upload_q(w), cache.k_pool, cache.v_pool, cache.page_table, plan)
+    check(f"non-causal {dtype} D={D} P={P.tolist()} L={L.tolist()}", out, oracle_out(w, oracle_pools(w), causal=False),
+          dtype)
+
+
 @pytest.mark.parametrize("splits", [1, 3, 8, 0])
 def test_decode_splits_agree(splits):
     w = wl.config5(decode_only=True).subset(range(6))

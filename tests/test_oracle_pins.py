@@ -143,6 +143,29 @@ def test_window_matches_sdpa_band_mask(window, P, L):
     assert np.abs(got - sdpa_full(w, window)).max() < 1e-12
 
 
+@pytest.mark.parametrize("P,L,hq,hkv,d,ps", [(0, 37, 2, 1, 8, 4), (30, 7, 4, 2, 16, 3), (17, 47, 3, 3, 4, 5)])
+def test_non_causal_matches_sdpa_without_mask(P, L, hq, hkv, d, ps):
+    """Non-causal: each chunk row attends to all N keys of its request, later
+    chunk rows included -- torch SDPA with no mask over the full sequence."""
+    w = tiny(P, L, hq=hq, hkv=hkv, d=d, ps=ps, config_id=250 + P)
+    got = oracle_out(w, oracle_pools(w), dtype=np.float64, causal=False)
+    N = P + L
+    k, v = w.kv_seq(0)
+    q = w.q_rows(0, P, N)
+    t = lambda a: torch.from_numpy(a.astype(np.float64)).permute(1, 0, 2)[None]  # noqa: E731
+    want = F.scaled_dot_product_attention(t(q), t(k), t(v), enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    assert np.abs(got - want).max() < 1e-12
+    # and it differs from the causal result wherever a row has later keys
+    causal = oracle_out(w, oracle_pools(w), dtype=np.float64)
+    assert np.abs(got[:-1] - causal[:-1]).max() > 1e-3 and np.abs(got[-1] - causal[-1]).max() < 1e-12
+
+
+def test_non_causal_zero_score_is_the_mean_of_all_values():
+    w = tiny(5, 11, hq=2, hkv=1, d=4, ps=4, zero_q=True, ramp_v=True, config_id=251)
+    got = oracle_out(w, oracle_pools(w), dtype=np.float64, causal=False)
+    assert np.array_equal(got, np.full_like(got, (16 + 1) / 2))   # v[t] = t + 1, t < 16
+
+
 def test_one_token_row_sees_every_key():
     """A one-token chunk after P cached tokens is plain softmax attention over all P+1 keys."""
     w = tiny(57, 1, hq=4, hkv=1, d=16, ps=8, config_id=401)
