@@ -12,7 +12,11 @@ Parity status of each function (what pins it is listed in the tests):
   extend_attention  pinned: zero-score closed forms (the PR's [1,2,3,4]),
                     torch scaled_dot_product_attention on the full sequence
                     (causal, GQA, band mask), W=1 and single-key identities,
-                    bitwise partition invariance
+                    bitwise partition invariance; non-causal: SDPA without a
+                    mask, zero-score mean of all values; explicit mask: an
+                    all-keep mask and the causal mask written out reproduce the
+                    unmasked results, SDPA with the same bool mask, broadcast
+                    axes, rows that keep nothing give 0
   rope_rows         pinned: identity, quarter and half turns (exact), the
                     hand-worked adjacent-pair example, complex multiplication,
                     norm preservation, angle composition and the relative-

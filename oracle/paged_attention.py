@@ -112,7 +112,8 @@ def visible_range(pos: int, window: int) -> Tuple[int, int]:
 def extend_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, page_table: np.ndarray,
                      prefix_lens: Sequence[int], chunk_lens: Sequence[int], window: int = 0,
                      sm_scale: Optional[float] = None, req_pool_indices: Optional[np.ndarray] = None,
-                     dtype=np.float32, rows: Optional[Iterable[int]] = None, causal: bool = True) -> np.ndarray:
+                     dtype=np.float32, rows: Optional[Iterable[int]] = None, causal: bool = True,
+                     mask: Optional[np.ndarray] = None) -> np.ndarray:
     """Attention output [total_q, Hq, D] for a ragged batch of chunks.
 
     ``q`` holds the chunk queries [total_q, Hq, D] in request order; the pools
@@ -120,7 +121,14 @@ def extend_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, page
     work to those global token indices (other rows are left NaN), for sampled
     checks of large batches. ``causal=False`` (AstrAI compare,
     attn_paged_prefill with is_causal=False: no causal offset) lets every row
-    see all N_b keys of its request, chunk rows after it included."""
+    see all N_b keys of its request, chunk rows after it included.
+
+    ``mask`` (same page: a bool mask, True = keep, 2-D [batch, kv_len] or 4-D
+    [batch, 1 or heads, 1 or q_len, kv_len]) is taken here as an array
+    [B, Hm, Qm, Ks] with Hm in {1, Hq} and Qm in {1, >= max chunk length}
+    (a size-1 axis is shared by every head or row; a 2-D mask is Hm = Qm = 1)
+    and Ks >= N_b, indexed by chunk row i and absolute key position j; a key
+    is visible if the mask keeps it *and* it is in the causal/window range."""
     q = np.asarray(q)
     total_q, hq, d = q.shape
     hkv = k_pool.shape[2]
@@ -152,12 +160,25 @@ def extend_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, page
             lo, hi = visible_range(P + i, window) if causal else (0, n)
             if hi <= lo:
                 continue                                    # no visible key -> 0
-            for kvh in range(hkv):
-                heads = slice(kvh * group, (kvh + 1) * group)   # query heads h with h // G == kvh
-                qv = q[t, heads].astype(dtype)                # [G, D]
-                keys = K[lo:hi, kvh]                          # [n_vis, D]
-                vals = V[lo:hi, kvh]
-                s = (qv @ keys.T) * scale                     # scores, [G, n_vis]
-                e = np.exp(s - s.max(axis=1, keepdims=True))
-                out[t, heads] = (e @ vals) / e.sum(axis=1, keepdims=True)
+            if mask is None:
+                for kvh in range(hkv):
+                    heads = slice(kvh * group, (kvh + 1) * group)   # query heads h with h // G == kvh
+                    qv = q[t, heads].astype(dtype)                # [G, D]
+                    keys = K[lo:hi, kvh]                          # [n_vis, D]
+                    vals = V[lo:hi, kvh]
+                    s = (qv @ keys.T) * scale                     # scores, [G, n_vis]
+                    e = np.exp(s - s.max(axis=1, keepdims=True))
+                    out[t, heads] = (e @ vals) / e.sum(axis=1, keepdims=True)
+                continue
+            # explicit mask: the kept keys of the range, per query head
+            mrow = i if mask.shape[2] > 1 else 0
+            for h in range(hq):
+                keep = np.nonzero(mask[b, h if mask.shape[1] > 1 else 0, mrow, lo:hi])[0] + lo
+                if keep.size == 0:
+                    continue                                # no visible key -> 0
+                kvh = h // group
+                qv = q[t, h].astype(dtype)
+                s = (K[keep, kvh] @ qv) * scale
+                e = np.exp(s - s.max())
+                out[t, h] = (e @ V[keep, kvh]) / e.sum()
     return out

@@ -34,12 +34,12 @@ def oracle_pools(w: wl.Workload, pools: Optional[Tuple[np.ndarray, np.ndarray]] 
 
 def oracle_out(w: wl.Workload, pools: Tuple[np.ndarray, np.ndarray], dtype=np.float32,
                rows: Optional[Sequence[int]] = None, sm_scale: Optional[float] = None,
-               causal: bool = True) -> np.ndarray:
+               causal: bool = True, mask: Optional[np.ndarray] = None) -> np.ndarray:
     kp, vp = pools
     q = wl.values(w.q_all(), w.dtype)
     return oracle.extend_attention(q, wl.values(kp, w.dtype), wl.values(vp, w.dtype), w.page_table,
                                    w.prefix_lens, w.chunk_lens, window=w.window, sm_scale=sm_scale,
-                                   dtype=dtype, rows=rows, causal=causal)
+                                   dtype=dtype, rows=rows, causal=causal, mask=mask)
 
 
 def parity_report(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float):

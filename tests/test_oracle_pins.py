@@ -166,6 +166,58 @@ def test_non_causal_zero_score_is_the_mean_of_all_values():
     assert np.array_equal(got, np.full_like(got, (16 + 1) / 2))   # v[t] = t + 1, t < 16
 
 
+def rand_mask(rng, B, hm, qm, ks, p=0.7):
+    m = (rng.random((B, hm, qm, ks)) < p).astype(np.uint8)
+    return m
+
+
+def test_mask_all_true_and_causal_mask_reproduce_the_unmasked_results():
+    w = tiny(9, 23, hq=4, hkv=2, d=16, ps=4, config_id=260)
+    pools = oracle_pools(w)
+    N = 9 + 23
+    ones = np.ones((1, 1, 1, N + 3), np.uint8)
+    # (the masked path evaluates head by head, the unmasked one a GQA group at once: same sums,
+    # another rounding order, so the comparison is in float64)
+    ref = oracle_out(w, pools, dtype=np.float64)
+    assert np.abs(oracle_out(w, pools, dtype=np.float64, causal=True, mask=ones) - ref).max() < 1e-12
+    # the causal mask written out, applied without the causal flag
+    cm = np.zeros((1, 1, 23, N), np.uint8)
+    for i in range(23):
+        cm[0, 0, i, :9 + i + 1] = 1
+    assert np.abs(oracle_out(w, pools, dtype=np.float64, causal=False, mask=cm) - ref).max() < 1e-12
+
+
+def test_mask_matches_sdpa_with_bool_mask():
+    """Random per-head, per-row mask (non-causal): torch SDPA with the same bool
+    attn_mask over the contiguous sequence, fp64 (every row keeps >= 1 key)."""
+    P, L, hq, hkv, d = 6, 21, 4, 2, 8
+    w = tiny(P, L, hq=hq, hkv=hkv, d=d, ps=4, config_id=261)
+    N = P + L
+    rng = np.random.default_rng(3)
+    m = rand_mask(rng, 1, hq, L, N + 5)
+    m[..., P] = 1                                   # every row keeps key P
+    got = oracle_out(w, oracle_pools(w), dtype=np.float64, causal=False, mask=m)
+    k, v = w.kv_seq(0)
+    q = w.q_rows(0, P, N)
+    t = lambda a: torch.from_numpy(a.astype(np.float64)).permute(1, 0, 2)[None]  # noqa: E731
+    am = torch.from_numpy(m[0, :, :, :N].astype(bool))[None]                      # [1, Hq, L, N]
+    want = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=am, enable_gqa=True)[0].permute(1, 0, 2)
+    assert np.abs(got - want.numpy()).max() < 1e-12
+
+
+def test_mask_broadcast_axes_and_empty_rows():
+    w = tiny(4, 10, hq=4, hkv=1, d=8, ps=4, config_id=262)
+    pools = oracle_pools(w)
+    rng = np.random.default_rng(4)
+    m2 = rand_mask(rng, 1, 1, 1, 16)                 # 2-D: one key mask for every head and row
+    full = np.broadcast_to(m2, (1, 4, 10, 16)).copy()
+    assert np.array_equal(oracle_out(w, pools, mask=m2), oracle_out(w, pools, mask=full))
+    m = np.ones((1, 4, 10, 16), np.uint8)
+    m[0, 2, 3, :] = 0                                # head 2 of row 3 keeps nothing -> 0
+    out = oracle_out(w, pools, mask=m, causal=False)
+    assert np.array_equal(out[3, 2], np.zeros(8, np.float32)) and np.abs(out[3, 1]).max() > 0
+
+
 def test_one_token_row_sees_every_key():
     """A one-token chunk after P cached tokens is plain softmax attention over all P+1 keys."""
     w = tiny(57, 1, hq=4, hkv=1, d=16, ps=8, config_id=401)
