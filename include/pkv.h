@@ -247,6 +247,32 @@ int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, con
                       const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
                       size_t workspace_bytes, pkv_stream_t stream);
 
+/*
+ * paged_extend_attn_masked -- paged_extend_attn with an explicit keep-mask
+ * (AstrAI compare v1.3.12..925cbed, attn_paged_prefill: a bool mask, True =
+ * keep, 2-D [batch, kv_len] or 4-D [batch, 1 or heads, 1 or q_len, kv_len],
+ * applied together with the causal flag).
+ *
+ * A key j of row i (chunk row, 0-based) of request b, query head h, is visible
+ * when it is visible for paged_extend_attn with the same plan (causal or not,
+ * window) and mask[((b * mask_heads + hh) * mask_rows + ii) * mask_kv_stride + j]
+ * is nonzero, with hh = h if mask_heads > 1 else 0 and ii = i if mask_rows > 1
+ * else 0 (a 2-D mask is mask_heads = mask_rows = 1). A row that keeps no key
+ * gets 0.
+ *   mask            device bytes, 4-byte aligned
+ *   mask_heads      1 or Hq
+ *   mask_rows       1 or >= plan->max_q_len
+ *   mask_kv_stride  bytes per mask row, a multiple of 4, >= plan->max_kv_len
+ * Every other argument and error as paged_extend_attn, plus
+ * PKV_ERR_INVALID_ARGUMENT for a NULL or malformed mask.
+ */
+int paged_extend_attn_masked(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                             const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                             const uint8_t* mask, int32_t mask_heads, int32_t mask_rows, int32_t mask_kv_stride,
+                             const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
+                             size_t workspace_bytes, pkv_stream_t stream);
+
 /* Copies the plan's device status word to *status_out after synchronising the
  * stream (a diagnostic; not needed on the hot path). */
 int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream);

@@ -9,6 +9,7 @@ stream. The functions carry the C names:
   pkv_append(k_new, v_new, k_pool, v_pool, page_table, plan)
   pkv_rope_append(q, k_new, v_new, rope_table, k_pool, v_pool, page_table, plan)
   paged_extend_attn(q, k_pool, v_pool, page_table, plan, out=None, ...)
+  paged_extend_attn_masked(q, k_pool, v_pool, page_table, plan, mask, out=None, ...)
 
 There is no fallback: if libpkv.so is missing, importing this package
 raises ImportError.
@@ -300,6 +301,43 @@ def paged_extend_attn(q, k_pool, v_pool, page_table, plan: ExtendPlan, out=None,
                                   float(sm_scale), ctypes.byref(plan.plan), ctypes.byref(s),
                                   ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes,
                                   _stream_handle(stream, q.device)), "paged_extend_attn")
+    return out
+
+
+def paged_extend_attn_masked(q, k_pool, v_pool, page_table, plan: ExtendPlan, mask, out=None,
+                             window: Optional[int] = None, sm_scale: float = 0.0, req_pool_indices=None,
+                             workspace=None, stream=None):
+    """paged_extend_attn with an explicit keep-mask: a bool or uint8 device
+    tensor [B, 1 or Hq, 1 or >= max_q_len, Ks] (Ks >= max_kv_len, a multiple
+    of 4), contiguous; nonzero keeps the (chunk row, absolute key) pair."""
+    import torch
+    s = plan.shape
+    dt = _torch_dtype(s.dtype)
+    tq = plan.plan.total_q
+    _expect(q, (tq, s.num_q_heads, s.head_dim), dt, "q")
+    _expect(k_pool, _pool_shape(s), dt, "k_pool")
+    _expect(v_pool, _pool_shape(s), dt, "v_pool")
+    _check_tables(page_table, plan, req_pool_indices)
+    if mask.dtype not in (torch.bool, torch.uint8) or mask.dim() != 4 or not mask.is_contiguous() \
+            or mask.shape[0] != plan.plan.batch or mask.device != q.device:
+        raise ValueError(f"mask: expected a contiguous bool/uint8 [{plan.plan.batch}, Hm, Qm, Ks] tensor on "
+                         f"{q.device}, got {mask.dtype} {tuple(mask.shape)} on {mask.device}")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, (tq, s.num_q_heads, s.head_dim), dt, "out")
+    if workspace is None:
+        workspace = plan.workspace()
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opt = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    _check(_lib.paged_extend_attn_masked(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_pool.data_ptr()),
+                                         ctypes.c_void_p(v_pool.data_ptr()), ctypes.c_void_p(page_table.data_ptr()),
+                                         page_table.shape[1], opt(req_pool_indices), None, None, None,
+                                         plan.plan.window if window is None else int(window), float(sm_scale),
+                                         ctypes.c_void_p(mask.data_ptr()), mask.shape[1], mask.shape[2],
+                                         mask.shape[3], ctypes.byref(plan.plan), ctypes.byref(s),
+                                         ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes,
+                                         _stream_handle(stream, q.device)), "paged_extend_attn_masked")
     return out
 
 

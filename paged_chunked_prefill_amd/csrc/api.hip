@@ -215,28 +215,45 @@ int pkv_rope_append(const void* q, void* q_out, const void* k_new, const void* v
   return launch_append(a, stream);
 }
 
-int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
-                      int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
-                      const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
-                      const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
-                      size_t workspace_bytes, pkv_stream_t stream) {
+static int extend_attn_call(const char* name, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, int32_t page_table_stride, const int32_t* req_pool_indices,
+                            const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* prefix_lens,
+                            int32_t window, float sm_scale, const uint8_t* mask, int32_t mask_heads,
+                            int32_t mask_rows, int32_t mask_kv_stride, const pkv_plan* plan, const pkv_shape* shape,
+                            void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
   g_error[0] = 0;
-  int st = check_plan(plan, shape, "paged_extend_attn");
+  int st = check_plan(plan, shape, name);
   if (st) return st;
-  if ((st = check_page_table(page_table, page_table_stride, plan, "paged_extend_attn"))) return st;
+  if ((st = check_page_table(page_table, page_table_stride, plan, name))) return st;
   if (window != plan->window)
-    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn: window %d differs from the plan's %d", window,
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: window %d differs from the plan's %d", name, window,
                      plan->window);
   if (plan->total_q > 0 && (!q || !k_pool || !v_pool || !out))
-    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn: q, pools and out must not be NULL");
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: q, pools and out must not be NULL", name);
   if (!(std::isfinite(sm_scale)))
-    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn: sm_scale is not finite");
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: sm_scale is not finite", name);
+  if (mask && plan->total_q > 0) {
+    if (mask_heads != 1 && mask_heads != shape->num_q_heads)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: mask_heads must be 1 or %d (got %d)", name,
+                       shape->num_q_heads, mask_heads);
+    if (mask_rows != 1 && mask_rows < plan->max_q_len)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: mask_rows must be 1 or >= the longest chunk %d (got %d)", name,
+                       plan->max_q_len, mask_rows);
+    if (mask_kv_stride < plan->max_kv_len || (mask_kv_stride & 3))
+      return set_error(PKV_ERR_INVALID_ARGUMENT,
+                       "%s: mask_kv_stride must be a multiple of 4 and >= the longest request %d (got %d)", name,
+                       plan->max_kv_len, mask_kv_stride);
+    if (reinterpret_cast<uintptr_t>(mask) & 3)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: mask must be 4-byte aligned", name);
+    if (int64_t(plan->batch) * mask_heads * mask_rows * int64_t(mask_kv_stride) >= (int64_t(1) << 40))
+      return set_error(PKV_ERR_UNSUPPORTED, "%s: mask too large", name);
+  }
   if (plan->workspace_bytes > 0) {
     if (!workspace)
-      return set_error(PKV_ERR_WORKSPACE, "paged_extend_attn: the plan needs %zu workspace bytes, got NULL",
+      return set_error(PKV_ERR_WORKSPACE, "%s: the plan needs %zu workspace bytes, got NULL", name,
                        plan->workspace_bytes);
     if (workspace_bytes < plan->workspace_bytes)
-      return set_error(PKV_ERR_WORKSPACE, "paged_extend_attn: workspace holds %zu bytes, %zu needed",
+      return set_error(PKV_ERR_WORKSPACE, "%s: workspace holds %zu bytes, %zu needed", name,
                        workspace_bytes, plan->workspace_bytes);
   }
   if ((st = check_current_device())) return st;
@@ -269,7 +286,36 @@ int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, con
   a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.shape = *shape;
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  a.mask_rows = mask_rows;
+  a.mask_kv_stride = mask_kv_stride;
   return launch_extend_attn(a, stream);
+}
+
+int paged_extend_attn(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                      int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                      const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                      const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
+                      size_t workspace_bytes, pkv_stream_t stream) {
+  return extend_attn_call("paged_extend_attn", q, k_pool, v_pool, page_table, page_table_stride, req_pool_indices,
+                          qo_indptr, kv_indptr, prefix_lens, window, sm_scale, nullptr, 1, 1, 0, plan, shape, out,
+                          workspace, workspace_bytes, stream);
+}
+
+int paged_extend_attn_masked(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                             const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                             const uint8_t* mask, int32_t mask_heads, int32_t mask_rows, int32_t mask_kv_stride,
+                             const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
+                             size_t workspace_bytes, pkv_stream_t stream) {
+  if (!mask && plan && plan->total_q > 0) {
+    g_error[0] = 0;
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "paged_extend_attn_masked: mask must not be NULL");
+  }
+  return extend_attn_call("paged_extend_attn_masked", q, k_pool, v_pool, page_table, page_table_stride,
+                          req_pool_indices, qo_indptr, kv_indptr, prefix_lens, window, sm_scale, mask, mask_heads,
+                          mask_rows, mask_kv_stride, plan, shape, out, workspace, workspace_bytes, stream);
 }
 
 int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream) {

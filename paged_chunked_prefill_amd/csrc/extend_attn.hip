@@ -73,7 +73,22 @@ struct Params {
   int32_t total_q;
   int32_t max_splits;
   float scale_log2;
+  // explicit keep-mask (only the MASK kernels read these): byte (b, h, i, j) at
+  // mask[((b * mask_heads + h) * mask_rows + i) * mask_kv_stride + j], a size-1
+  // head or row axis shared; i is the chunk row, j the absolute key position
+  const uint8_t* mask;
+  int32_t mask_heads;
+  int32_t mask_rows;
+  int32_t mask_kv_stride;
+  const int32_t* qo_indptr;
 };
+
+// Byte offset of the mask row of (request, query head, chunk row).
+__device__ inline int64_t mask_row_offset(const Params& p, int req, int head, int chunk_row) {
+  const int h = p.mask_heads > 1 ? head : 0;
+  const int i = p.mask_rows > 1 ? chunk_row : 0;
+  return (int64_t(req * p.mask_heads + h) * p.mask_rows + i) * p.mask_kv_stride;
+}
 
 // Value of the same query row held by the other half of the wave (lanes l and
 // l^32 hold the two halves of one row's scores).
@@ -210,7 +225,7 @@ __device__ __forceinline__ void pin_m_schedule() {
   if constexpr (ST + 1 < NSTEP) pin_m_schedule<ST + 1, NSTEP, AHEAD>();
 }
 
-template <int D, bool POW2_PAGES>
+template <int D, bool POW2_PAGES, bool MASK>
 __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
@@ -364,15 +379,45 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // wait for LDS reads and for every gather but the newest, then the block barrier.
   // The LDS/scalar wait comes first on its own so that it stays on every path
   // (the compiler then knows no scalar load is pending after a barrier).
-  auto sync = [&]() __attribute__((always_inline)) {
+  // EXTRA more loads may stay in flight: the keep-mask loads issued after the
+  // newest gather (MASK only, see below).
+  auto sync = [&](auto extra_c) __attribute__((always_inline)) {
+    constexpr int EXTRA = decltype(extra_c)::value;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (POW2_PAGES && newest_issued)
-      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * T::LOADS>);
+      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * T::LOADS + EXTRA>);
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+  };
+
+  // Keep-mask (MASK): the 32 mask bytes of this lane's row for a tile, as 8
+  // words (key block kb2, group g: keys kv0 + 32kb2 + 8g + 4half .. +3, the
+  // order of the score accumulator), loaded one tile ahead with loads the
+  // compiler does not see (a compiler-visible load would make its first use
+  // wait for every gather in flight). They are issued right after the newest
+  // gather's copies and before the next ones, so the barrier waits below cover
+  // them; each word array is pinned (an empty asm that "writes" it) after such
+  // a wait, before its first use. Group starts outside the item's key range
+  // are clamped into it (4-byte aligned): those keys are masked by the range.
+  constexpr int kMaskWords = 8;
+  uint32_t mw_cur[kMaskWords], mw_next[kMaskWords];
+  const uint8_t* mrow = nullptr;
+  if constexpr (MASK)
+    mrow = p.mask + mask_row_offset(p, it.req, head, it.tok0 + (row_live ? tok : 0) - p.qo_indptr[it.req]);
+  auto mask_issue = [&](int u, uint32_t* w) __attribute__((always_inline)) {
+    const int kvb4 = it.kv_begin & ~3, kvl4 = (it.kv_end - 1) & ~3;
+#pragma unroll
+    for (int k = 0; k < kMaskWords; ++k) {
+      const int gs = min(max(t0 + u * T::BC + 32 * (k >> 2) + 8 * (k & 3) + 4 * half, kvb4), kvl4);
+      asm volatile("global_load_dword %0, %1, off" : "=v"(w[k]) : "v"(mrow + gs));
+    }
+  };
+  auto mask_pin = [&](uint32_t* w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kMaskWords; ++k) asm volatile("" : "+v"(w[k]));
   };
 
   // prologue part 1: the item's Q rows gathered into LDS like the K rows (same
@@ -408,6 +453,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       prepare(ids[u], t0 + u * T::BC, stage_of(u), cp);
 #pragma unroll
       for (int c2 = 0; c2 < 2 * T::LOADS; ++c2) issue(cp, c2);
+      if (MASK && u == 0) mask_issue(0, mw_cur);   // landed with tile 0 at the wait below
     }
     newest_issued = true;
   }
@@ -421,6 +467,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if (MASK && ntiles > 0) mask_pin(mw_cur);
   // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7]
   bf16x8 qf[T::KSTEPS];
 #pragma unroll
@@ -444,7 +491,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   auto seg_V = [&](int t) __attribute__((always_inline)) {
     const int kv0 = t0 + t * T::BC;
     // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
-    const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
+    const bool full = !MASK && kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
                       (window <= 0 || kv0 > qpos_last - window);
     if (!full) {
       // this row sees keys lo..hi of the item's range (one unsigned test per key)
@@ -457,7 +504,9 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (uint32_t(d0 + 32 * kb2 + 8 * (j >> 2) + (j & 3)) > width) s[kb2][j] = -INFINITY;
+          if (uint32_t(d0 + 32 * kb2 + 8 * (j >> 2) + (j & 3)) > width ||
+              (MASK && ((mw_cur[4 * kb2 + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0))
+            s[kb2][j] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -541,10 +590,11 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   };
 
   // prologue part 2: S(0), group 1 one segment behind
+  constexpr auto kNoExtra = std::integral_constant<int, 0>{};
   if (ntiles > 0) {
-    if (grp == 1) sync();
+    if (grp == 1) sync(kNoExtra);
     if (wave_live) seg_S0();
-    sync();
+    sync(kNoExtra);
   }
   // tile t: segments V(t) and M(t) = PV(t) + S(t+1). The gather of tile t+3 goes
   // with slot 2t+2: group 1 issues it before its V segment, group 0 before its M
@@ -555,17 +605,26 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // which keeps the segment free of branches; they are waited for below.
   for (int t = 0; t < ntiles; ++t) {
     const bool last = t + 1 >= ntiles;
+    if constexpr (MASK) {
+      // tile t's words (loaded one iteration ago, waited for by the last barrier), then tile t+1's
+      if (t > 0) {
+        mask_pin(mw_next);
+#pragma unroll
+        for (int k = 0; k < kMaskWords; ++k) mw_cur[k] = mw_next[k];
+      }
+      mask_issue(t + 1, mw_next);
+    }
     fetch_pages(pg, t0 + (t + 3) * T::BC);
     if (wave_live) seg_V(t);
     prepare(pg, t0 + (t + 3) * T::BC, stage_of(t + 3), cp);   // addresses only: nothing is written yet
-    sync();
+    sync(std::integral_constant<int, MASK ? kMaskWords : 0>{});   // tile t+2's copies and the mask loads may fly
     if (wave_live) {
       seg_M(t);
     } else {
 #pragma unroll
       for (int c2 = 0; c2 < NCOPY; ++c2) issue(cp, c2);
     }
-    if (!last || grp == 0) sync();
+    if (!last || grp == 0) sync(kNoExtra);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // no copy into LDS outlives the workgroup
   if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
@@ -626,7 +685,7 @@ struct F32Tile {
   static constexpr int DBLK = D / 32;
 };
 
-template <int D>
+template <int D, bool MASK>
 __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
   using T = F32Tile<D>;
   __shared__ float smem[2 * T::STAGE];
@@ -642,6 +701,10 @@ __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
   const int qpos = it.pos0 + tok;
   const int head = it.kv_head * G + gh;
   const bool wave_live = wave * 32 < it.q_count * G;
+  // this row's keep-mask bytes (a row past the item reads the item's first row)
+  const uint8_t* mrow = nullptr;
+  if constexpr (MASK)
+    mrow = p.mask + mask_row_offset(p, it.req, head, it.tok0 + (row_live ? tok : 0) - p.qo_indptr[it.req]);
 
   // Q operand: lane holds q[row][2ks + half]
   float qf[T::KSTEPS];
@@ -718,7 +781,7 @@ __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = kv0 + 8 * (j >> 2) + 4 * half + (j & 3);
-        if (!key_visible(key, qpos, it.kv_begin, it.kv_end, p.window)) s[j] = -INFINITY;
+        if (!key_visible(key, qpos, it.kv_begin, it.kv_end, p.window) || (MASK && !mrow[key])) s[j] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -878,13 +941,24 @@ void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
       // the rows of one wave-wide gather share a page when the page size is a
       // power of two of at least that many rows
       const int ps = a.shape.page_size;
-      if ((ps & (ps - 1)) == 0 && ps >= Bf16Tile<D>::RPI)
-        hipLaunchKernelGGL((extend_attn_bf16<D, true>), dim3(a.n_items), dim3(64 * kWavesBf16), 0, st, p);
+      const dim3 grid(a.n_items), block(64 * kWavesBf16);
+      if ((ps & (ps - 1)) == 0 && ps >= Bf16Tile<D>::RPI) {
+        if (a.mask)
+          hipLaunchKernelGGL((extend_attn_bf16<D, true, true>), grid, block, 0, st, p);
+        else
+          hipLaunchKernelGGL((extend_attn_bf16<D, true, false>), grid, block, 0, st, p);
+      } else {
+        if (a.mask)
+          hipLaunchKernelGGL((extend_attn_bf16<D, false, true>), grid, block, 0, st, p);
+        else
+          hipLaunchKernelGGL((extend_attn_bf16<D, false, false>), grid, block, 0, st, p);
+      }
+    } else {
+      if (a.mask)
+        hipLaunchKernelGGL((extend_attn_f32<D, true>), dim3(a.n_items), dim3(256), 0, st, p);
       else
-        hipLaunchKernelGGL((extend_attn_bf16<D, false>), dim3(a.n_items), dim3(64 * kWavesBf16), 0, st, p);
+        hipLaunchKernelGGL((extend_attn_f32<D, false>), dim3(a.n_items), dim3(256), 0, st, p);
     }
-    else
-      hipLaunchKernelGGL(extend_attn_f32<D>, dim3(a.n_items), dim3(256), 0, st, p);
   }
   if (a.n_split_rows > 0) {
     CombineParams cp;
@@ -927,6 +1001,11 @@ int launch_extend_attn(const AttnArgs& a, void* stream) {
   p.total_q = a.total_q;
   p.max_splits = a.max_splits;
   p.scale_log2 = a.scale_log2;
+  p.mask = a.mask;
+  p.mask_heads = a.mask_heads;
+  p.mask_rows = a.mask_rows;
+  p.mask_kv_stride = a.mask_kv_stride;
+  p.qo_indptr = a.qo_indptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = a.shape.dtype == PKV_DTYPE_BF16;
   if (a.shape.head_dim == 128) {

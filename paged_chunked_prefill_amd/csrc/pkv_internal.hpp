@@ -128,6 +128,9 @@ struct AttnArgs {
   int32_t window;
   float scale_log2;   // softmax scale * log2(e)
   pkv_shape shape;
+  // explicit keep-mask, or nullptr: bytes [B][mask_heads][mask_rows][mask_kv_stride]
+  const uint8_t* mask = nullptr;
+  int32_t mask_heads = 1, mask_rows = 1, mask_kv_stride = 0;
 };
 
 int launch_extend_attn(const AttnArgs& a, void* stream);

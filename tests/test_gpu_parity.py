@@ -377,3 +377,72 @@ def test_empty_chunks_only():
     out = pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan)
     torch.cuda.synchronize()
     assert out.shape == (0, 4, 64)
+
+
+# ---------------------------------------------------------------------------
+# explicit keep-mask (paged_extend_attn_masked)
+# ---------------------------------------------------------------------------
+
+def _masked_case(dtype, P, L, hq, hkv, D, ps, mh, mr, causal, seed, p_keep=0.6, splits=0, empty_row=None):
+    P, L = np.array(P, np.int32), np.array(L, np.int32)
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 4
+    pt = wl.shuffled_page_table(seed, pages, P + L, ps)
+    w = wl.Workload("masked", 8, dtype, hq, hkv, D, ps, pages, 0, P, L, pt)
+    ks = int(((P + L).max() + 3) // 4 * 4) + 4
+    rows = 1 if mr == 1 else int(L.max())
+    rng = np.random.default_rng(seed)
+    m = (rng.random((len(L), mh, rows, ks)) < p_keep).astype(np.uint8)
+    if empty_row is not None:
+        b, h, i = empty_row
+        m[b, h, i] = 0
+    cache = DeviceCache(w)
+    cache.fill_prefix(w)
+    plan = pkv.build_extend_metadata(P, L, shape_of(w), 0, splits, device="cuda", causal=causal)
+    kn, vn = cache._gather_new_kv(w)
+    pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan)
+    md = torch.from_numpy(m).to("cuda")
+    out = pkv.paged_extend_attn_masked(upload_q(w), cache.k_pool, cache.v_pool, cache.page_table, plan, md)
+    torch.cuda.synchronize()
+    assert pkv.read_status(plan) == 0
+    return values_of(out), oracle_out(w, oracle_pools(w), causal=causal, mask=m), m
+
+
+@pytest.mark.parametrize("dtype,P,L,hq,hkv,D,ps,mh,mr,causal", [
+    ("bf16", [0, 100, 513], [64, 128, 1], 16, 4, 128, 16, 16, 128, True),    # per head and row, ragged + 1-token row
+    ("bf16", [0, 0], [256, 128], 32, 4, 128, 64, 1, 256, False),             # the pages' [batch, 1, q_len, kv_len]
+    ("bf16", [37, 5], [90, 200], 8, 2, 64, 16, 1, 1, True),                   # 2-D [batch, kv_len]
+    ("bf16", [20, 7], [45, 60], 6, 3, 128, 3, 6, 60, True),                   # pages of 3 tokens (general gather)
+    ("fp32", [10, 0], [40, 33], 4, 2, 64, 16, 4, 40, True),
+    ("fp32", [0], [70], 2, 1, 128, 5, 1, 70, False),
+])
+def test_masked(dtype, P, L, hq, hkv, D, ps, mh, mr, causal):
+    got, ref, _ = _masked_case(dtype, P, L, hq, hkv, D, ps, mh, mr, causal, seed=11)
+    assert not np.isnan(got).any()
+    check(f"masked {dtype} D={D} ps={ps} mask[{mh},{mr}] causal={causal}", got, ref, dtype)
+
+
+def test_masked_split_rows_and_an_empty_row():
+    # one-token rows split 8 ways over long ranges; head 3 of row 0 of request 1 keeps nothing -> 0
+    got, ref, _ = _masked_case("bf16", [3000, 1500, 0], [1, 1, 64], 16, 4, 128, 16, 16, 64, True, seed=12,
+                               splits=8, empty_row=(1, 3, 0))
+    check("masked split rows", got, ref, "bf16")
+    assert np.array_equal(got[1, 3], np.zeros(128, np.float32))
+
+
+def test_causal_mask_written_out_equals_the_causal_plan():
+    """The causal mask given explicitly to a non-causal plan gives the causal
+    result (the pages' 4-D causal-mask regression)."""
+    P, L = np.array([0, 64], np.int32), np.array([200, 130], np.int32)
+    ps, hq, hkv, D = 16, 8, 2, 128
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 4
+    w = wl.Workload("causalmask", 9, "bf16", hq, hkv, D, ps, pages, 0, P, L, wl.shuffled_page_table(9, pages, P + L, ps))
+    ks = 272                     # >= the longest request (264), a multiple of 4
+    m = np.zeros((2, 1, 200, ks), np.uint8)
+    for b in range(2):
+        for i in range(int(L[b])):
+            m[b, 0, i, :int(P[b]) + i + 1] = 1
+    out_c, cache, plan_c = prefill_and_attend(w)
+    plan_n = pkv.build_extend_metadata(P, L, shape_of(w), 0, 0, device="cuda", causal=False)
+    out_m = pkv.paged_extend_attn_masked(upload_q(w), cache.k_pool, cache.v_pool, cache.page_table, plan_n,
+                                         torch.from_numpy(m).to("cuda"))
+    check("causal mask on a non-causal plan", out_m, values_of(out_c), "bf16")
