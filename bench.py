@@ -110,6 +110,9 @@ def main():
                     help="also time the step replayed from captured HIP graphs (append + attention per batch, "
                          "metadata built once), reported as graph_replay")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows for the CPU oracle sample (0: auto)")
+    ap.add_argument("--mask", choices=["none", "rows", "heads"], default="none",
+                    help="run paged_extend_attn_masked with an all-keep mask of [B, 1, max_q_len, Ks] (rows) or "
+                         "[B, Hq, max_q_len, Ks] (heads): same visible pairs, so the TFLOP/s show the mask's cost")
     ap.add_argument("--rope", action="store_true",
                     help="the step rotates q and k at their absolute positions with pkv_rope_append (in place "
                          "of pkv_append) before the attention; reports that kernel's HBM rate")
@@ -197,16 +200,27 @@ def main():
                                 cache.page_table.shape[1], None, ctypes.byref(plan), ctypes.byref(shape), sh)
             b["append_bytes"] = int(L.sum()) * 4 * esize * w.head_dim * w.num_kv_heads
         q_attn = b["q_rot"] if args.rope else q
-        b["attn_args"] = (vp(q_attn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table), cache.page_table.shape[1],
-                          None, None, None, None, bw.window, 0.0, ctypes.byref(plan), ctypes.byref(shape), vp(out),
-                          vp(ws), ws.numel(), sh)
+        if args.mask == "none":
+            b["attn_fn"] = lib.paged_extend_attn
+            b["attn_args"] = (vp(q_attn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
+                              cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, ctypes.byref(plan),
+                              ctypes.byref(shape), vp(out), vp(ws), ws.numel(), sh)
+        else:
+            ks = (int((P + L).max()) + 3) // 4 * 4
+            mh = w.num_q_heads if args.mask == "heads" else 1
+            b["mask"] = torch.ones((len(L), mh, int(L.max()), ks), dtype=torch.uint8, device=dev)
+            b["attn_fn"] = lib.paged_extend_attn_masked
+            b["attn_args"] = (vp(q_attn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
+                              cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, vp(b["mask"]), mh,
+                              int(L.max()), ks, ctypes.byref(plan), ctypes.byref(shape), vp(out), vp(ws), ws.numel(),
+                              sh)
         B.append(b)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in B]
           for _ in range(nsteps)]
-    build, attn = lib.build_extend_metadata, lib.paged_extend_attn
+    build = lib.build_extend_metadata
 
     def step(s):
         for i, b in enumerate(B):
@@ -215,7 +229,7 @@ def main():
             if b["append_fn"](*b["append_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
             ev[s][i][0].record(stream)
-            if attn(*b["attn_args"]):
+            if b["attn_fn"](*b["attn_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
             ev[s][i][1].record(stream)
 
@@ -290,7 +304,8 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
-        "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope), "batches_per_step": len(B),
+        "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope),
+                   "explicit_mask": args.mask, "batches_per_step": len(B),
                    "query_tokens_per_step": tokens, "flops_per_step": flops},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
@@ -328,12 +343,12 @@ def time_graph_replay(args, B, lib, flops, tokens):
         at = b["attn_args"][:-1] + (sh,)
         torch.cuda.synchronize()
         with torch.cuda.stream(s):       # one eager pass on the capture stream first
-            if b["append_fn"](*ap) or lib.paged_extend_attn(*at):
+            if b["append_fn"](*ap) or b["attn_fn"](*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            if b["append_fn"](*ap) or lib.paged_extend_attn(*at):
+            if b["append_fn"](*ap) or b["attn_fn"](*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
         graphs.append(g)
     for _ in range(args.warmup):
