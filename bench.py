@@ -491,7 +491,7 @@ def cpu_baseline(w, batches, sample_rows):
     except Exception:  # noqa: BLE001
         cores = len(os.sched_getaffinity(0))
     last = batches[-1]
-    if len(batches) > 1:                        # chunked prompt: the whole prompt as one full prefill
+    if len(batches) > 1 and last.batch == 1:    # chunked prompt: the whole prompt as one full prefill
         full = last.with_lengths([0], [int(last.kv_lens[0])])
         pool_w = full
     else:
