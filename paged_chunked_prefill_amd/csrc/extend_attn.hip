@@ -37,6 +37,7 @@
 
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "pkv_internal.hpp"
 
@@ -207,6 +208,18 @@ struct Bf16Tile {
   static __device__ int vswz(int r) { return CH == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// Keep-mask helpers (MASK instantiation). Word K of a lane's tile holds the
+// mask bytes of keys 32(K/4) + 8(K%4) + 4half .. +3 after the lane's tile
+// base: loads the compiler does not see (see the kernel), with the offsets as
+// immediates.
+template <int K>
+__device__ __forceinline__ void load_mask_word(uint32_t& w, const uint8_t* a) {
+  asm volatile("global_load_dword %0, %1, off offset:%2" : "=v"(w) : "v"(a), "n"(32 * (K >> 2) + 8 * (K & 3)));
+}
+template <int... K>
+__device__ __forceinline__ void load_mask_words(uint32_t* w, const uint8_t* a, std::integer_sequence<int, K...>) {
+  (load_mask_word<K>(w[K], a), ...);
+}
 // Issue order of the MFMA segment (see seg_M below): PV and S steps
 // alternate (even steps PV, odd steps S), each one MFMA whose A fragment was
 // read from LDS AHEAD steps earlier (two transposing reads for PV, one b128 read
@@ -409,10 +422,16 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     mrow = p.mask + mask_row_offset(p, it.req, head, it.tok0 + (row_live ? tok : 0) - p.qo_indptr[it.req]);
   auto mask_issue = [&](int u, uint32_t* w) __attribute__((always_inline)) {
     const int kvb4 = it.kv_begin & ~3, kvl4 = (it.kv_end - 1) & ~3;
+    const int kv0u = t0 + u * T::BC;
+    if (kv0u >= kvb4 && kv0u + T::BC - 4 <= kvl4) {
+      // (uniform) every word of the tile lies in the range: one address, immediate offsets
+      load_mask_words(w, mrow + kv0u + 4 * half, std::make_integer_sequence<int, kMaskWords>{});
+    } else {
 #pragma unroll
-    for (int k = 0; k < kMaskWords; ++k) {
-      const int gs = min(max(t0 + u * T::BC + 32 * (k >> 2) + 8 * (k & 3) + 4 * half, kvb4), kvl4);
-      asm volatile("global_load_dword %0, %1, off" : "=v"(w[k]) : "v"(mrow + gs));
+      for (int k = 0; k < kMaskWords; ++k) {
+        const int gs = min(max(kv0u + 32 * (k >> 2) + 8 * (k & 3) + 4 * half, kvb4), kvl4);
+        asm volatile("global_load_dword %0, %1, off" : "=v"(w[k]) : "v"(mrow + gs));
+      }
     }
   };
   auto mask_pin = [&](uint32_t* w) __attribute__((always_inline)) {
@@ -491,9 +510,16 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   auto seg_V = [&](int t) __attribute__((always_inline)) {
     const int kv0 = t0 + t * T::BC;
     // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
-    const bool full = !MASK && kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
+    const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
                       (window <= 0 || kv0 > qpos_last - window);
-    if (!full) {
+    if (MASK && full) {
+      // every key of the tile is in range for every row: the keep-mask alone
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (((mw_cur[4 * kb2 + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0) s[kb2][j] = -INFINITY;
+    } else if (!full) {
       // this row sees keys lo..hi of the item's range (one unsigned test per key)
       int lo = it.kv_begin, hi = min(kv_last, qpos);
       if (window > 0) lo = max(lo, qpos - window + 1);
