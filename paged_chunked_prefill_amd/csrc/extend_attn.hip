@@ -887,20 +887,24 @@ struct CombineParams {
 
 // One row of 32 lanes per (split row, query head), two rows per wave: each
 // lane owns VEC = D/32 consecutive output values and loads them with one
-// 8- or 16-byte read per split. Lane j < ns of a row also holds split j's
-// (max, sum); 32 lanes cover every split count a plan can have.
+// 8- or 16-byte read per split. Every lane of a row also reads every split's
+// (max, sum) -- the same addresses across the row, so one request each -- and
+// merges on its own: no exchange between lanes, and the first PF splits'
+// values go out together with their (max, sum), right after the row's split
+// count. PF is 2, 4 or 8 by the launch's largest split count (up to 16
+// splits the rows past 8 take two more short rounds), 32 above that.
 template <int D>
 struct CombineShape {
   static constexpr int LANES = 32;
   static constexpr int ROWS = 2;
   static constexpr int VEC = D / 32;
-  static_assert(PKV_MAX_SPLITS <= LANES, "one lane per split");
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, int PF>
 __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
   using C = CombineShape<D>;
   typedef float fvec __attribute__((ext_vector_type(C::VEC)));
+  typedef uint16_t hvec __attribute__((ext_vector_type(C::VEC)));
   const int lane = threadIdx.x & 63;
   const int sub = lane / C::LANES, j = lane % C::LANES;      // row within the wave, lane within the row
   const int wid = (blockIdx.x * 4 + (threadIdx.x >> 6)) * C::ROWS + sub;
@@ -910,19 +914,8 @@ __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
   const int token = p.split_rows[2 * slot];
   const int ns = min(p.split_rows[2 * slot + 1], p.max_splits);
   const int64_t base = (int64_t(slot) * p.num_q_heads + head) * p.max_splits;
-  const float mk = j < ns ? p.ml_part[(base + j) * 2] : -INFINITY;
-  const float lk = j < ns ? p.ml_part[(base + j) * 2 + 1] : 0.f;
-  // max and weighted sum over the row's lanes (xor shuffles stay inside the row)
-  float M = mk;
-#pragma unroll
-  for (int o = C::LANES / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float wk = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
-  float den = wk * lk;
-#pragma unroll
-  for (int o = C::LANES / 2; o > 0; o >>= 1) den += __shfl_xor(den, o);
-  fvec acc = {};
+  const float2* ml = reinterpret_cast<const float2*>(p.ml_part) + base;
   // lane j's VEC elements of split k's partial row
-  typedef uint16_t hvec __attribute__((ext_vector_type(C::VEC)));
   auto part = [&](int k) __attribute__((always_inline)) {
     if constexpr (BF16) {
       const hvec h = reinterpret_cast<const hvec*>(static_cast<const uint16_t*>(p.o_part) + base * D)[k * C::LANES + j];
@@ -934,29 +927,67 @@ __global__ __launch_bounds__(256) void combine_splits(const CombineParams p) {
       return reinterpret_cast<const fvec*>(static_cast<const float*>(p.o_part) + base * D)[k * C::LANES + j];
     }
   };
-  const int row0 = sub * C::LANES;   // first lane of this row
-  int k = 0;
-  for (; k + 4 <= ns; k += 4) {      // four splits' loads in flight
-    fvec v[4];
-    float wt[4];
+  // Loads past the row's split count read its last split again (in bounds,
+  // no branch around the loads) and get weight 0.
+  const int klast = max(ns - 1, 0);
+  fvec v[PF];
+  float2 mlk[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    mlk[u] = ml[min(u, klast)];
+    v[u] = part(min(u, klast));
+  }
+  // the row's reference: the largest split max
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < PF; ++u) M = fmaxf(M, mlk[u].x);   // (the repeated last split changes nothing)
+  for (int k = PF; k < ns; k += 4) {
+    float2 mm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mm[u] = ml[min(k + u, klast)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) M = fmaxf(M, mm[u].x);
+  }
+  auto weight = [&](float mk, bool in) __attribute__((always_inline)) {
+    return in && mk != -INFINITY ? fast_exp2(mk - M) : 0.f;
+  };
+  fvec acc = {};
+  float den = 0.f;
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    const float wk = weight(mlk[u].x, u < ns);
+    den += wk * mlk[u].y;
+    acc += wk * v[u];
+  }
+  for (int k = PF; k < ns; k += 4) {   // more splits (long one-token rows): four in flight
+    fvec vv[4];
+    float2 mm[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      v[u] = part(k + u);
-      wt[u] = __shfl(wk, row0 + k + u);
+      mm[u] = ml[min(k + u, klast)];
+      vv[u] = part(min(k + u, klast));
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += wt[u] * v[u];
+    for (int u = 0; u < 4; ++u) {
+      const float wk = weight(mm[u].x, k + u < ns);
+      den += wk * mm[u].y;
+      acc += wk * vv[u];
+    }
   }
-  for (; k < ns; ++k) acc += __shfl(wk, row0 + k) * part(k);
   if (!live || token < 0 || token >= p.total_q) return;
   if (!(den > 0.f)) den = INFINITY;  // no visible key: output 0
   const int64_t orow = (int64_t(token) * p.num_q_heads + head) * D + C::VEC * j;
+  if constexpr (BF16) {
+    typedef __bf16 bvec __attribute__((ext_vector_type(C::VEC)));
+    bvec o;
 #pragma unroll
-  for (int x = 0; x < C::VEC; ++x) {
-    if (BF16)
-      static_cast<__bf16*>(p.out)[orow + x] = (__bf16)(acc[x] / den);
-    else
-      static_cast<float*>(p.out)[orow + x] = acc[x] / den;
+    for (int x = 0; x < C::VEC; ++x) o[x] = (__bf16)(acc[x] / den);
+    *reinterpret_cast<bvec*>(static_cast<__bf16*>(p.out) + orow) = o;
+  } else {
+    fvec o;
+#pragma unroll
+    for (int x = 0; x < C::VEC; ++x) o[x] = acc[x] / den;
+    *reinterpret_cast<fvec*>(static_cast<float*>(p.out) + orow) = o;
   }
 }
 
@@ -997,8 +1028,15 @@ void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
     cp.max_splits = a.max_splits;
     cp.total_q = a.total_q;
     const int rows_per_block = 4 * CombineShape<D>::ROWS;
-    hipLaunchKernelGGL((combine_splits<D, BF16>), dim3((cp.n_rows + rows_per_block - 1) / rows_per_block), dim3(256),
-                       0, st, cp);
+    const dim3 grid((cp.n_rows + rows_per_block - 1) / rows_per_block), block(256);
+    if (cp.max_splits <= 2)
+      hipLaunchKernelGGL((combine_splits<D, BF16, 2>), grid, block, 0, st, cp);
+    else if (cp.max_splits <= 4)
+      hipLaunchKernelGGL((combine_splits<D, BF16, 4>), grid, block, 0, st, cp);
+    else if (cp.max_splits <= 16)
+      hipLaunchKernelGGL((combine_splits<D, BF16, 8>), grid, block, 0, st, cp);
+    else
+      hipLaunchKernelGGL((combine_splits<D, BF16, PKV_MAX_SPLITS>), grid, block, 0, st, cp);
   }
 }
 

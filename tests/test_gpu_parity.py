@@ -248,7 +248,7 @@ def test_non_causal(dtype, P, L, hq, hkv, D):
           dtype)
 
 
-@pytest.mark.parametrize("splits", [1, 3, 8, 0])
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 12, 0])
 def test_decode_splits_agree(splits):
     w = wl.config5(decode_only=True).subset(range(6))
     out, _, plan = prefill_and_attend(w, decode_splits=splits)
