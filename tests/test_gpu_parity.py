@@ -286,6 +286,42 @@ def test_variants(dtype, D, hq, hkv, ps, window):
     check(f"variant {dtype} D={D} {hq}/{hkv} ps={ps} W={window}", out, oracle_out(w, oracle_pools(w)), dtype)
 
 
+# Short chunks and one-token rows whose rows all fit one 16-row block
+# (max_q_len * G <= 16), with splits, windows and small pages.
+@pytest.mark.parametrize("hq,hkv,ps,P,L,window,splits", [
+    (8, 2, 16, [0, 37, 500, 130, 64], [1, 1, 1, 4, 2], 0, 0),
+    (4, 4, 64, [0, 100, 999, 63], [16, 3, 1, 16], 0, 0),
+    (16, 2, 4, [77, 0, 300], [2, 1, 2], 50, 0),
+    (16, 1, 16, [1000, 5], [1, 1], 0, 5),
+    (4, 2, 32, [0, 129, 64, 7], [8, 5, 1, 0], 0, 3),
+    (8, 2, 64, [4095, 1, 2000], [1, 4, 3], 130, 12),
+    (4, 1, 8, [0, 0], [4, 1], 0, 0),
+])
+def test_one_block_items(hq, hkv, ps, P, L, window, splits):
+    P, L = np.array(P, np.int32), np.array(L, np.int32)
+    assert int(L.max()) * (hq // hkv) <= 16
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 3
+    w = wl.Workload("one-block", 44, "bf16", hq, hkv, 128, ps, pages, window, P, L,
+                    wl.shuffled_page_table(44, pages, P + L, ps), decode_splits=splits)
+    out, _, plan = prefill_and_attend(w)
+    assert pkv.read_status(plan) == 0
+    check(f"one-block G={hq // hkv} ps={ps} L={L.tolist()} W={window} splits={splits}", out,
+          oracle_out(w, oracle_pools(w)), "bf16")
+
+
+def test_one_block_zero_score_exact():
+    """Zero scores on one-token rows with splits: every output is the mean of the values 1..N."""
+    P = np.array([999, 2047, 77, 0], np.int32)
+    L = np.array([1, 1, 1, 1], np.int32)
+    w = wl.Workload("zs-one-block", 45, "bf16", 8, 2, 128, 16, 512, 0, P, L,
+                    wl.shuffled_page_table(45, 512, P + L, 16), zero_q=True, ramp_v=True, decode_splits=4)
+    out, _, plan = prefill_and_attend(w)
+    want = (P.astype(np.float64) + 2) / 2          # mean of 1..N
+    got = values_of(out)[:, :, :]
+    ref = np.broadcast_to(want[:, None, None], got.shape)
+    check("one-block zero scores", out, ref.astype(np.float32), "bf16")
+
+
 def test_one_row_longest_range_most_splits():
     """One token after 131071 cached keys, split the most ways the ABI allows
     (32), next to a short row: sampled against the oracle row by row."""
