@@ -129,7 +129,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build is single-GPU only (paged extend attention on one MI355X); "
+        print("bench.py: runs on one GPU only (paged extend attention on one MI355X; no multi-GPU path); "
               f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
         sys.exit(2)
 
