@@ -41,6 +41,38 @@ HBM_PEAK = 8000.0            # GB/s
 # workloads: a list of batches run in order against one cache
 # ---------------------------------------------------------------------------
 
+class HipEvents:
+    """Timing events recorded straight through the HIP runtime (one ctypes call
+    per record): the per-launch brackets of the timed steps then add about a
+    microsecond of host time each instead of a torch.cuda.Event round trip, so
+    that they do not stretch a host-bound step."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+        self.record = self.hip.hipEventRecord
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
 def workload(name):
     import workloads as wl
     if name.startswith("prompt"):
@@ -218,33 +250,45 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in B]
-          for _ in range(nsteps)]
+    hev = HipEvents(2 * nsteps * len(B))   # (step s, batch i): events 2(s*len(B)+i) and +1
+    evs, rec = hev.ev, hev.record
     build = lib.build_extend_metadata
 
-    def step(s):
+    def step(s, bracket):
         for i, b in enumerate(B):
             if build(*b["meta_args"][s]):
                 raise RuntimeError(lib.pkv_last_error().decode())
             if b["append_fn"](*b["append_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
-            ev[s][i][0].record(stream)
+            k = 2 * (s * len(B) + i)
+            if bracket:
+                rec(evs[k], sh)
             if b["attn_fn"](*b["attn_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
-            ev[s][i][1].record(stream)
+            if bracket:
+                rec(evs[k + 1], sh)
 
     for s in range(args.warmup):
-        step(s)
+        step(s, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.warmup, nsteps):
-        step(s)
+        step(s, False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
+    # Launch durations: the same K steps again (same plans, appends and attention
+    # calls), each attention call bracketed by HIP events on its stream. The timed
+    # steps above carry no events: on these launch-bound steps every event marker
+    # between two kernels costs GPU time (the headline step measures about 25 %
+    # longer with them).
+    for s in range(args.warmup, nsteps):
+        step(s, True)
+    torch.cuda.synchronize()
 
-    attn_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.warmup, nsteps)) / args.steps
-               for i in range(len(B))]
+    attn_ms = [sum(hev.elapsed_ms(2 * (s * len(B) + i), 2 * (s * len(B) + i) + 1)
+                   for s in range(args.warmup, nsteps)) / args.steps for i in range(len(B))]
+    hev.close()
     # the appends (or rotary appends) of a step, timed in a pass of their own after the timed steps so that
     # their events do not add to the step (rewriting the same slots and q rows: idempotent)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -275,6 +319,7 @@ def main():
         "unit": "GB/s" if decode_bound else "TFLOP/s",
         "frac": None, "traffic": None,
         "avg_launch_us": round(1e3 * attn_total_ms / n_launch, 3),
+        "launch_timing": "HIP events around every attention call of a second pass over the same K steps",
         "launches_per_step": n_launch,
         "algorithmic_per_launch": round((hbm_bytes if decode_bound else flops) / n_launch),
     }
