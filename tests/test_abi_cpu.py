@@ -7,6 +7,8 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import oracle
 import paged_chunked_prefill_amd as pkv
@@ -129,6 +131,61 @@ def test_work_list_covers_every_row_once(cfg):
         s, splits = shape(12, 4, 64, 16, 1024), 0
     p = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, s, w.window, splits)
     coverage(p, w.prefix_lens, w.chunk_lens, s.num_q_heads, s.num_kv_heads, w.window)
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.data())
+def test_work_list_coverage_random(data):
+    """Random batches (ragged prefixes and chunks, empty chunks, one-token rows,
+    GQA groups, windows, page sizes, explicit split counts): the coverage
+    invariants above hold for every plan."""
+    B = data.draw(st.integers(1, 6))
+    P = np.array(data.draw(st.lists(st.integers(0, 3000), min_size=B, max_size=B)), np.int32)
+    L = np.array(data.draw(st.lists(st.sampled_from([0, 1, 1, 2, 5, 17, 64, 65, 255, 300]),
+                                    min_size=B, max_size=B)), np.int32)
+    if int(L.sum()) == 0:
+        L[0] = 1
+    hkv = data.draw(st.sampled_from([1, 2, 4, 8]))
+    hq = hkv * data.draw(st.sampled_from([1, 2, 3, 4, 8, 16]))
+    window = data.draw(st.sampled_from([0, 0, 1, 7, 64, 500]))
+    splits = data.draw(st.sampled_from([0, 0, 1, 3, 8, pkv.PKV_MAX_SPLITS]))
+    ps = data.draw(st.sampled_from([1, 3, 16, 64]))
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 1
+    s = shape(hq, hkv, 128, ps, pages)
+    p = pkv.build_extend_metadata(P, L, s, window, splits)
+    coverage(p, P, L, hq, hkv, window)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.data())
+def test_non_causal_plan_random(data):
+    """Random non-causal batches: every (request, query tile, KV head) key range,
+    merged over its splits, is exactly the request's [0, N_b), contiguous and
+    disjoint, and every chunk row of every head is covered."""
+    B = data.draw(st.integers(1, 5))
+    P = np.array(data.draw(st.lists(st.integers(0, 2000), min_size=B, max_size=B)), np.int32)
+    L = np.array(data.draw(st.lists(st.sampled_from([0, 1, 3, 64, 100, 257]), min_size=B, max_size=B)), np.int32)
+    if int(L.sum()) == 0:
+        L[-1] = 3
+    hkv = data.draw(st.sampled_from([1, 2, 4]))
+    hq = hkv * data.draw(st.sampled_from([1, 4, 8]))
+    splits = data.draw(st.sampled_from([0, 2, 8]))
+    ps = data.draw(st.sampled_from([1, 16, 64]))
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 1
+    p = pkv.build_extend_metadata(P, L, shape(hq, hkv, 128, ps, pages), 0, splits, causal=False)
+    it = p.host_sections()["items"]
+    assert (it["pos0"] == 1 << 30).all()
+    ranges, rows = {}, set()
+    for x in it:
+        b = int(x["req"])
+        ranges.setdefault((b, int(x["q_begin"]), int(x["kv_head"])), []).append((int(x["kv_begin"]), int(x["kv_end"])))
+        for t in range(int(x["q_begin"]), int(x["q_begin"]) + int(x["q_count"])):
+            rows.add((b, t, int(x["kv_head"])))
+    for (b, _, _), rs in ranges.items():
+        rs.sort()
+        assert rs[0][0] == 0 and rs[-1][1] == P[b] + L[b], rs
+        assert all(a[1] == c[0] and a[0] < a[1] for a, c in zip(rs, rs[1:])), rs
+    assert rows == {(b, t, h) for b in range(B) for t in range(int(L[b])) for h in range(hkv)}
 
 
 def test_config5_split_plan():
