@@ -133,7 +133,7 @@ def test_work_list_covers_every_row_once(cfg):
     coverage(p, w.prefix_lens, w.chunk_lens, s.num_q_heads, s.num_kv_heads, w.window)
 
 
-@settings(max_examples=80, deadline=None)
+@settings(max_examples=80, deadline=None, derandomize=True, database=None)
 @given(st.data())
 def test_work_list_coverage_random(data):
     """Random batches (ragged prefixes and chunks, empty chunks, one-token rows,
@@ -156,7 +156,7 @@ def test_work_list_coverage_random(data):
     coverage(p, P, L, hq, hkv, window)
 
 
-@settings(max_examples=60, deadline=None)
+@settings(max_examples=60, deadline=None, derandomize=True, database=None)
 @given(st.data())
 def test_non_causal_plan_random(data):
     """Random non-causal batches: every (request, query tile, KV head) key range,

@@ -8,6 +8,8 @@ bytewise, NaN canaries included)."""
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import oracle
 import workloads as wl
@@ -320,6 +322,35 @@ def test_one_block_zero_score_exact():
     got = values_of(out)[:, :, :]
     ref = np.broadcast_to(want[:, None, None], got.shape)
     check("one-block zero scores", out, ref.astype(np.float32), "bf16")
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None)
+@given(st.data())
+def test_random_batches(data):
+    """Random small batches (a fixed, derandomized set): ragged prefixes and
+    chunks (empty chunks and one-token rows among them), bf16 or fp32, D 64 or
+    128, GQA groups, page sizes, windows and split counts, against the oracle."""
+    dtype = data.draw(st.sampled_from(["bf16", "bf16", "fp32"]))
+    D = data.draw(st.sampled_from([64, 128]))
+    B = data.draw(st.integers(1, 4))
+    P = np.array(data.draw(st.lists(st.integers(0, 700), min_size=B, max_size=B)), np.int32)
+    L = np.array(data.draw(st.lists(st.sampled_from([0, 1, 1, 3, 16, 33, 64, 100]), min_size=B, max_size=B)),
+                 np.int32)
+    if int(L.sum()) == 0:
+        L[0] = 1
+    hkv = data.draw(st.sampled_from([1, 2, 4]))
+    hq = hkv * data.draw(st.sampled_from([1, 2, 4, 8]))
+    ps = data.draw(st.sampled_from([1, 4, 16, 64]))
+    window = data.draw(st.sampled_from([0, 0, 1, 50]))
+    splits = data.draw(st.sampled_from([0, 0, 2, 7]))
+    seed = data.draw(st.integers(0, 1000))
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 2
+    w = wl.Workload("random", 46, dtype, hq, hkv, D, ps, pages, window, P, L,
+                    wl.shuffled_page_table(seed, pages, P + L, ps), decode_splits=splits)
+    out, _, plan = prefill_and_attend(w)
+    assert pkv.read_status(plan) == 0
+    check(f"random {dtype} D={D} {hq}/{hkv} ps={ps} W={window} splits={splits} P={P.tolist()} L={L.tolist()}",
+          out, oracle_out(w, oracle_pools(w)), dtype)
 
 
 def test_one_row_longest_range_most_splits():
