@@ -488,6 +488,33 @@ def test_masked(dtype, P, L, hq, hkv, D, ps, mh, mr, causal):
     check(f"masked {dtype} D={D} ps={ps} mask[{mh},{mr}] causal={causal}", got, ref, dtype)
 
 
+@settings(max_examples=30, deadline=None, derandomize=True, database=None)
+@given(st.data())
+def test_masked_random(data):
+    """Random keep-masks (a fixed, derandomized set) over random small batches:
+    dtype, head dim, GQA, page sizes (general gather included), mask head and
+    row axes shared or not, causal or not, keep rates from almost none to all,
+    split counts."""
+    dtype = data.draw(st.sampled_from(["bf16", "bf16", "fp32"]))
+    D = data.draw(st.sampled_from([64, 128]))
+    B = data.draw(st.integers(1, 3))
+    P = data.draw(st.lists(st.integers(0, 400), min_size=B, max_size=B))
+    L = data.draw(st.lists(st.sampled_from([1, 2, 17, 64, 90]), min_size=B, max_size=B))
+    hkv = data.draw(st.sampled_from([1, 2]))
+    hq = hkv * data.draw(st.sampled_from([1, 4]))
+    ps = data.draw(st.sampled_from([3, 16, 64]))
+    mh = data.draw(st.sampled_from([1, hq]))
+    mr = data.draw(st.sampled_from([1, 2]))   # 1: shared row axis; else one row per chunk row
+    causal = data.draw(st.booleans())
+    p_keep = data.draw(st.sampled_from([0.05, 0.5, 0.95, 1.0]))
+    splits = data.draw(st.sampled_from([0, 3]))
+    seed = data.draw(st.integers(0, 1000))
+    got, ref, _ = _masked_case(dtype, P, L, hq, hkv, D, ps, mh, mr, causal, seed=seed, p_keep=p_keep, splits=splits)
+    assert not np.isnan(got).any()
+    check(f"masked random {dtype} D={D} {hq}/{hkv} ps={ps} mask[{mh},{mr}] causal={causal} keep={p_keep} "
+          f"splits={splits} P={P} L={L}", got, ref, dtype)
+
+
 def test_masked_split_rows_and_an_empty_row():
     # one-token rows split 8 ways over long ranges; head 3 of row 0 of request 1 keeps nothing -> 0
     got, ref, _ = _masked_case("bf16", [3000, 1500, 0], [1, 1, 64], 16, 4, 128, 16, 16, 64, True, seed=12,
