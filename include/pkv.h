@@ -273,6 +273,32 @@ int paged_extend_attn_masked(const void* q, const void* k_pool, const void* v_po
                              const pkv_plan* plan, const pkv_shape* shape, void* out, void* workspace,
                              size_t workspace_bytes, pkv_stream_t stream);
 
+/*
+ * paged_extend_attn_append -- steps a2..a9 in one call: pkv_append of the
+ * chunk's K/V and paged_extend_attn over the result (AReno PR #642: the chunk
+ * continues inside its request's last page and attends to the cached prefix;
+ * AstrAI compare, cache.py and the backend's prefill path: the step's K/V are
+ * written to the slots of positions start_pos .. seq_len-1, then the paged
+ * attention reads the cache). Output and every pool byte equal those of
+ * pkv_append followed by paged_extend_attn, bit for bit.
+ * bf16: a single attention launch does both. Its gather reads key positions
+ * >= P_b from k_new / v_new rather than from the pool, and each new row is
+ * copied into its slot by the one work item whose query tile holds that token
+ * and whose key range holds its position (split-row combine as usual).
+ * fp32: the append kernel runs first, then the attention.
+ *   k_new, v_new   [total_q, Hkv, D]; must not overlap the pools
+ *   k_pool, v_pool read at positions < P_b, written at P_b .. N_b - 1
+ * The batch offsets are the plan's (qo_indptr, kv_indptr, prefix_lens).
+ * Every other argument as paged_extend_attn. Errors as pkv_append and
+ * paged_extend_attn, plus PKV_ERR_INVALID_ARGUMENT when k_new or v_new
+ * overlaps a pool. A page id outside the pool sets PKV_STATUS_BAD_PAGE and that
+ * row is not written.
+ */
+int paged_extend_attn_append(const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                             const int32_t* page_table, int32_t page_table_stride, const int32_t* req_pool_indices,
+                             int32_t window, float sm_scale, const pkv_plan* plan, const pkv_shape* shape,
+                             void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
 /* Copies the plan's device status word to *status_out after synchronising the
  * stream (a diagnostic; not needed on the hot path). */
 int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream);

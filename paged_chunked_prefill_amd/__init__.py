@@ -10,6 +10,7 @@ stream. The functions carry the C names:
   pkv_rope_append(q, k_new, v_new, rope_table, k_pool, v_pool, page_table, plan)
   paged_extend_attn(q, k_pool, v_pool, page_table, plan, out=None, ...)
   paged_extend_attn_masked(q, k_pool, v_pool, page_table, plan, mask, out=None, ...)
+  paged_extend_attn_append(q, k_new, v_new, k_pool, v_pool, page_table, plan, out=None, ...)
 
 There is no fallback: if libpkv.so is missing, importing this package
 raises ImportError.
@@ -301,6 +302,39 @@ def paged_extend_attn(q, k_pool, v_pool, page_table, plan: ExtendPlan, out=None,
                                   float(sm_scale), ctypes.byref(plan.plan), ctypes.byref(s),
                                   ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes,
                                   _stream_handle(stream, q.device)), "paged_extend_attn")
+    return out
+
+
+def paged_extend_attn_append(q, k_new, v_new, k_pool, v_pool, page_table, plan: ExtendPlan, out=None,
+                             window: Optional[int] = None, sm_scale: float = 0.0, req_pool_indices=None,
+                             workspace=None, stream=None):
+    """pkv_append of the chunk's K/V rows ([total_q, Hkv, D]) and the attention
+    over the result, in one call (one attention launch for bf16)."""
+    import torch
+    s = plan.shape
+    dt = _torch_dtype(s.dtype)
+    tq = plan.plan.total_q
+    _expect(q, (tq, s.num_q_heads, s.head_dim), dt, "q")
+    _expect(k_new, (tq, s.num_kv_heads, s.head_dim), dt, "k_new")
+    _expect(v_new, (tq, s.num_kv_heads, s.head_dim), dt, "v_new")
+    _expect(k_pool, _pool_shape(s), dt, "k_pool")
+    _expect(v_pool, _pool_shape(s), dt, "v_pool")
+    _check_tables(page_table, plan, req_pool_indices)
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, (tq, s.num_q_heads, s.head_dim), dt, "out")
+    if workspace is None:
+        workspace = plan.workspace()
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.paged_extend_attn_append(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+        ctypes.c_void_p(k_pool.data_ptr()), ctypes.c_void_p(v_pool.data_ptr()),
+        ctypes.c_void_p(page_table.data_ptr()), page_table.shape[1],
+        ctypes.c_void_p(req_pool_indices.data_ptr()) if req_pool_indices is not None else None,
+        plan.plan.window if window is None else int(window), float(sm_scale), ctypes.byref(plan.plan),
+        ctypes.byref(s), ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes, _stream_handle(stream, q.device)),
+        "paged_extend_attn_append")
     return out
 
 

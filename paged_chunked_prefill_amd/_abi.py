@@ -17,7 +17,8 @@ PKV_MAX_SPLITS = 32
 
 EXPORTS = ("pkv_extend_metadata_size", "build_extend_metadata", "pkv_extend_metadata_size_ex",
            "build_extend_metadata_ex", "pkv_append", "pkv_rope_append",
-           "paged_extend_attn", "paged_extend_attn_masked", "pkv_read_status", "pkv_last_error",
+           "paged_extend_attn", "paged_extend_attn_masked", "paged_extend_attn_append", "pkv_read_status",
+           "pkv_last_error",
            "pkv_device_supported")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P, _SZ, _P],
         "paged_extend_attn_masked": [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, ctypes.c_float, _P, _I32, _I32,
                                      _I32, ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P, _SZ, _P],
+        "paged_extend_attn_append": [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, ctypes.c_float,
+                                     ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P, _SZ, _P],
         "pkv_read_status": [ctypes.POINTER(PkvPlan), ctypes.POINTER(_I32), _P],
         "pkv_last_error": [],
         "pkv_device_supported": [ctypes.c_int],

@@ -220,7 +220,8 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
                             const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* prefix_lens,
                             int32_t window, float sm_scale, const uint8_t* mask, int32_t mask_heads,
                             int32_t mask_rows, int32_t mask_kv_stride, const pkv_plan* plan, const pkv_shape* shape,
-                            void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+                            void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream,
+                            const void* k_new = nullptr, const void* v_new = nullptr) {
   g_error[0] = 0;
   int st = check_plan(plan, shape, name);
   if (st) return st;
@@ -290,6 +291,12 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
   a.mask_heads = mask_heads;
   a.mask_rows = mask_rows;
   a.mask_kv_stride = mask_kv_stride;
+  if (k_new) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool_w = const_cast<void*>(k_pool);
+    a.v_pool_w = const_cast<void*>(v_pool);
+  }
   return launch_extend_attn(a, stream);
 }
 
@@ -316,6 +323,44 @@ int paged_extend_attn_masked(const void* q, const void* k_pool, const void* v_po
   return extend_attn_call("paged_extend_attn_masked", q, k_pool, v_pool, page_table, page_table_stride,
                           req_pool_indices, qo_indptr, kv_indptr, prefix_lens, window, sm_scale, mask, mask_heads,
                           mask_rows, mask_kv_stride, plan, shape, out, workspace, workspace_bytes, stream);
+}
+
+int paged_extend_attn_append(const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                             const int32_t* page_table, int32_t page_table_stride, const int32_t* req_pool_indices,
+                             int32_t window, float sm_scale, const pkv_plan* plan, const pkv_shape* shape,
+                             void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+  static const char* name = "paged_extend_attn_append";
+  g_error[0] = 0;
+  int st = check_plan(plan, shape, name);
+  if (st) return st;
+  if (plan->total_q > 0) {
+    if (!k_new || !v_new || !k_pool || !v_pool)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: K/V pointers must not be NULL", name);
+    // the launch reads k_new / v_new while it writes the pools
+    const size_t esize = shape->dtype == PKV_DTYPE_BF16 ? 2 : 4;
+    const size_t row = size_t(shape->num_kv_heads) * shape->head_dim * esize;
+    const size_t new_bytes = size_t(plan->total_q) * row;
+    const size_t pool_bytes = size_t(shape->num_pages) * size_t(shape->page_size) * row;
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+      const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+      return x < y + nb && y < x + na;
+    };
+    for (const void* n : {k_new, v_new})
+      for (const void* pl : {static_cast<const void*>(k_pool), static_cast<const void*>(v_pool)})
+        if (overlap(n, new_bytes, pl, pool_bytes))
+          return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: k_new / v_new overlap a pool", name);
+  }
+  if (shape->dtype != PKV_DTYPE_BF16) {
+    if ((st = pkv_append(k_new, v_new, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, plan, shape,
+                         stream)))
+      return st;
+    return extend_attn_call(name, q, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, nullptr,
+                            nullptr, nullptr, window, sm_scale, nullptr, 1, 1, 0, plan, shape, out, workspace,
+                            workspace_bytes, stream);
+  }
+  return extend_attn_call(name, q, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, nullptr, nullptr,
+                          nullptr, window, sm_scale, nullptr, 1, 1, 0, plan, shape, out, workspace, workspace_bytes,
+                          stream, plan->total_q > 0 ? k_new : nullptr, v_new);
 }
 
 int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream) {

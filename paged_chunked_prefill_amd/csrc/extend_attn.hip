@@ -82,6 +82,13 @@ struct Params {
   int32_t mask_rows;
   int32_t mask_kv_stride;
   const int32_t* qo_indptr;
+  // fused append (FUSED kernels only): the chunk's own K/V rows [total_q][Hkv][D],
+  // read by the gather for positions >= P_b and copied into their pool slots
+  const void* k_new;
+  const void* v_new;
+  void* k_pool_w;
+  void* v_pool_w;
+  const int32_t* prefix_lens;
 };
 
 // Byte offset of the mask row of (request, query head, chunk row).
@@ -238,9 +245,10 @@ __device__ __forceinline__ void pin_m_schedule() {
   if constexpr (ST + 1 < NSTEP) pin_m_schedule<ST + 1, NSTEP, AHEAD>();
 }
 
-template <int D, bool POW2_PAGES, bool MASK>
+template <int D, bool POW2_PAGES, bool MASK, bool FUSED>
 __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Params p) {
   using T = Bf16Tile<D>;
+  static_assert(!(MASK && FUSED), "the fused append has no masked form");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
   const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char*)smem));
 
@@ -278,6 +286,22 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   const uint32_t page_bytes = uint32_t(ps) * row_bytes;          // < 2^31, checked on the host
   const int kv_last = it.kv_end - 1;
 
+  // Fused append (FUSED): key positions >= P_b are the chunk's own rows. The
+  // gather reads them from k_new / v_new (position P_b + i is token
+  // qo_indptr[b] + i there), never from the pool slots this launch is filling;
+  // the owner item of each new row (below) copies it into its slot.
+  int fresh0 = INT_MAX;        // P_b: first position read from k_new / v_new
+  int tile_pos = 0;            // position of the tile's first token
+  const char* knew = nullptr;  // K row of position P_b (all KV heads)
+  const char* vnew = nullptr;
+  if constexpr (FUSED) {
+    fresh0 = ((const __attribute__((address_space(4))) int32_t*)p.prefix_lens)[it.req];
+    const int qs = ((const __attribute__((address_space(4))) int32_t*)p.qo_indptr)[it.req];
+    tile_pos = fresh0 + (it.tok0 - qs);
+    knew = static_cast<const char*>(p.k_new) + int64_t(qs) * row_bytes;
+    vnew = static_cast<const char*>(p.v_new) + int64_t(qs) * row_bytes;
+  }
+
   // Gather: wave w's copy i fills LDS rows RPI*(NW*i+w) .. +RPI-1 of a tile; lane l
   // covers row RPI*(NW*i+w) + l/CH at LDS chunk l%CH, i.e. source chunk (l%CH) ^ swz(row).
   // Both swizzles depend on the row only modulo CH, the same for every i. A key
@@ -307,8 +331,9 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
         ids[i] = pt[page_col(clampk(blk + lrow))];
     }
   };
-  // One wave-wide copy of RPI key rows of K and of V: with POW2_PAGES a scalar
-  // base and a lane offset each, else a full lane address each.
+  // One wave-wide copy of RPI key rows of K and of V: with POW2_PAGES (unfused) a
+  // scalar base and a lane offset each, else a full lane address each (a fused
+  // copy may take some rows from the pool and the rest from k_new / v_new).
   struct Copy {
     const char* k;
     const char* v;
@@ -322,7 +347,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       const bool ok = uint32_t(page) < uint32_t(p.num_pages);
       bad_page |= !ok;
       cp[i].dst = stage_lds + T::RPI * (T::NW * i + wave) * T::ROWB;  // first row of this copy
-      if (POW2_PAGES) {
+      if (POW2_PAGES && !FUSED) {
         const uint32_t off = __umul24(uint32_t(j & (ps - 1)), row_bytes);
         const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes;
         cp[i].k = ok ? kpool + pbase : reinterpret_cast<const char*>(g_zero_rows);
@@ -330,11 +355,16 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
         cp[i].koff = ok ? off + src_k : 16u * lane;
         cp[i].voff = ok ? off + src_v : 16u * lane;
       } else {
-        const int slot = j - (j / ps) * ps;
+        const int slot = POW2_PAGES ? (j & (ps - 1)) : j - (j / ps) * ps;
         const uint64_t pbase = uint64_t(uint32_t(ok ? page : 0)) * page_bytes + uint32_t(slot) * row_bytes;
         const char* zero = reinterpret_cast<const char*>(g_zero_rows) + 16 * lane;
         cp[i].k = ok ? kpool + pbase + src_k : zero;
         cp[i].v = ok ? vpool + pbase + src_v : zero;
+        if (FUSED && j >= fresh0) {   // a row of this chunk: straight from k_new / v_new
+          const int64_t r = int64_t(j - fresh0) * row_bytes;
+          cp[i].k = knew + r + src_k;
+          cp[i].v = vnew + r + src_v;
+        }
         cp[i].koff = cp[i].voff = 0;
       }
     }
@@ -342,7 +372,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   // copy c of a prepared tile: K rows for even c, V rows for odd c
   auto issue = [&](const Copy* cp, int c) __attribute__((always_inline)) {
     const Copy& x = cp[c >> 1];
-    if (POW2_PAGES) {
+    if (POW2_PAGES && !FUSED) {
       if (c & 1) lds_copy16(x.v, x.voff, x.dst + T::TILEB); else lds_copy16(x.k, x.koff, x.dst);
     } else {
       if (c & 1) lds_copy16(x.v, x.dst + T::TILEB); else lds_copy16(x.k, x.dst);
@@ -439,6 +469,66 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     for (int k = 0; k < kMaskWords; ++k) asm volatile("" : "+v"(w[k]));
   };
 
+  // Fused append: this item owns the new rows of its KV head at the positions of
+  // its own tokens that fall in its key range (each new row lies in exactly one
+  // split of the tile holding its token). The first OWN_TOK of them are loaded
+  // with tile 0 (loads the compiler does not see, so the prologue's wait covers
+  // them without waiting for tiles 1-2) and stored after that wait; any rest
+  // (more than OWN_TOK tokens per tile: G < 4 at D = 128) after the tile loop.
+  // Lane vector v: token v / (2 VPR), K for the first VPR vectors, then V.
+  constexpr int VPR = D * 2 / 16;                        // 16-byte vectors of one head's row
+  constexpr int NOWN = 4;                                // vectors per lane in the prologue copy
+  constexpr int OWN_VECS = 64 * kWavesBf16 * NOWN;
+  int own_lo = 0, own_n = 0;
+  if constexpr (FUSED) {
+    own_lo = max(it.kv_begin, tile_pos);
+    own_n = max(0, min(it.kv_end, tile_pos + it.q_count) - own_lo);
+  }
+  struct OwnVec {
+    const char* src;
+    char* dst;    // pool slot, page not yet applied
+    int col;      // page-table column of the row
+  };
+  auto own_vec = [&](int v) __attribute__((always_inline)) {
+    const int t = v / (2 * VPR), rem = v - t * (2 * VPR);
+    const bool isv = rem >= VPR;
+    const int e = isv ? rem - VPR : rem;
+    const int pos = own_lo + t;
+    const int64_t head_off = int64_t(it.kv_head) * D * 2 + 16 * e;
+    OwnVec o;
+    o.src = (isv ? vnew : knew) + int64_t(pos - fresh0) * row_bytes + head_off;
+    o.col = page_col(pos);
+    const int slot = pos - o.col * ps;
+    o.dst = static_cast<char*>(isv ? p.v_pool_w : p.k_pool_w) + int64_t(slot) * row_bytes + head_off;
+    return o;
+  };
+  u32x4 own_data[NOWN];
+  int own_page[NOWN];
+  auto own_issue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < NOWN; ++r) {
+      if (64 * kWavesBf16 * r < own_n * 2 * VPR) {   // (uniform)
+        const int v = min(tid + 64 * kWavesBf16 * r, own_n * 2 * VPR - 1);
+        const OwnVec o = own_vec(v);
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(own_data[r]) : "v"(o.src));
+        asm volatile("global_load_dword %0, %1, off" : "=v"(own_page[r]) : "v"(pt + o.col));
+      }
+    }
+  };
+  auto own_store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < NOWN; ++r) {
+      if (64 * kWavesBf16 * r < own_n * 2 * VPR) {
+        asm volatile("" : "+v"(own_data[r]), "+v"(own_page[r]));   // landed: waited for above
+        const int v = tid + 64 * kWavesBf16 * r;
+        const bool ok = uint32_t(own_page[r]) < uint32_t(p.num_pages);
+        bad_page |= !ok;
+        if (v < own_n * 2 * VPR && ok)
+          *reinterpret_cast<u32x4*>(own_vec(v).dst + int64_t(own_page[r]) * page_bytes) = own_data[r];
+      }
+    }
+  };
+
   // prologue part 1: the item's Q rows gathered into LDS like the K rows (same
   // copy shape and swizzle; rows past the item read the item's first token:
   // finite, never stored), issued first.
@@ -473,6 +563,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
 #pragma unroll
       for (int c2 = 0; c2 < 2 * T::LOADS; ++c2) issue(cp, c2);
       if (MASK && u == 0) mask_issue(0, mw_cur);   // landed with tile 0 at the wait below
+      if (FUSED && u == 0) own_issue();            // likewise
     }
     newest_issued = true;
   }
@@ -487,6 +578,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   if (MASK && ntiles > 0) mask_pin(mw_cur);
+  if (FUSED && ntiles > 0) own_store();
   // Q fragments (B operand of S^T = K Q^T): lane holds q[row][16ks + 8half .. +7]
   bf16x8 qf[T::KSTEPS];
 #pragma unroll
@@ -653,6 +745,16 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     if (!last || grp == 0) sync(kNoExtra);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // no copy into LDS outlives the workgroup
+  if constexpr (FUSED) {
+    // owned rows past the prologue's share (plain loads and stores)
+    for (int v = tid + OWN_VECS; v < own_n * 2 * VPR; v += 64 * kWavesBf16) {
+      const OwnVec o = own_vec(v);
+      const int page = pt[o.col];
+      const bool ok = uint32_t(page) < uint32_t(p.num_pages);
+      bad_page |= !ok;
+      if (ok) *reinterpret_cast<u32x4*>(o.dst + int64_t(page) * page_bytes) = *reinterpret_cast<const u32x4*>(o.src);
+    }
+  }
   if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) atomicOr(p.status, PKV_STATUS_BAD_PAGE);
 
   if (!wave_live) return;
@@ -999,16 +1101,21 @@ void launch_typed(const Params& p, const AttnArgs& a, hipStream_t st) {
       // power of two of at least that many rows
       const int ps = a.shape.page_size;
       const dim3 grid(a.n_items), block(64 * kWavesBf16);
+      const bool fused = a.k_new != nullptr;
       if ((ps & (ps - 1)) == 0 && ps >= Bf16Tile<D>::RPI) {
         if (a.mask)
-          hipLaunchKernelGGL((extend_attn_bf16<D, true, true>), grid, block, 0, st, p);
+          hipLaunchKernelGGL((extend_attn_bf16<D, true, true, false>), grid, block, 0, st, p);
+        else if (fused)
+          hipLaunchKernelGGL((extend_attn_bf16<D, true, false, true>), grid, block, 0, st, p);
         else
-          hipLaunchKernelGGL((extend_attn_bf16<D, true, false>), grid, block, 0, st, p);
+          hipLaunchKernelGGL((extend_attn_bf16<D, true, false, false>), grid, block, 0, st, p);
       } else {
         if (a.mask)
-          hipLaunchKernelGGL((extend_attn_bf16<D, false, true>), grid, block, 0, st, p);
+          hipLaunchKernelGGL((extend_attn_bf16<D, false, true, false>), grid, block, 0, st, p);
+        else if (fused)
+          hipLaunchKernelGGL((extend_attn_bf16<D, false, false, true>), grid, block, 0, st, p);
         else
-          hipLaunchKernelGGL((extend_attn_bf16<D, false, false>), grid, block, 0, st, p);
+          hipLaunchKernelGGL((extend_attn_bf16<D, false, false, false>), grid, block, 0, st, p);
       }
     } else {
       if (a.mask)
@@ -1070,6 +1177,11 @@ int launch_extend_attn(const AttnArgs& a, void* stream) {
   p.mask_rows = a.mask_rows;
   p.mask_kv_stride = a.mask_kv_stride;
   p.qo_indptr = a.qo_indptr;
+  p.k_new = a.k_new;
+  p.v_new = a.v_new;
+  p.k_pool_w = a.k_pool_w;
+  p.v_pool_w = a.v_pool_w;
+  p.prefix_lens = a.prefix_lens;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = a.shape.dtype == PKV_DTYPE_BF16;
   if (a.shape.head_dim == 128) {

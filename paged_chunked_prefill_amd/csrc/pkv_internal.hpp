@@ -131,6 +131,12 @@ struct AttnArgs {
   // explicit keep-mask, or nullptr: bytes [B][mask_heads][mask_rows][mask_kv_stride]
   const uint8_t* mask = nullptr;
   int32_t mask_heads = 1, mask_rows = 1, mask_kv_stride = 0;
+  // fused append (bf16 only): the chunk's K/V rows, also written into the pools
+  // by the attention launch itself; nullptr for the plain attention
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  void* k_pool_w = nullptr;
+  void* v_pool_w = nullptr;
 };
 
 int launch_extend_attn(const AttnArgs& a, void* stream);
