@@ -35,6 +35,7 @@ COPY_BYTES = 256 << 20       # bytes read and written per copy_calibration launc
 MFMA_PEAK_BF16 = 2500.0      # TFLOP/s, MI355X dense bf16
 MFMA_PEAK_FP32 = 157.3       # TFLOP/s, MI355X fp32 matrix (vector figure as stated for the chip)
 HBM_PEAK = 8000.0            # GB/s
+FUSE_MAX_SLOT_BLOCKS = 128   # paged_extend_attn_append fuses the append up to this plan.slot_blocks
 
 
 # ---------------------------------------------------------------------------
@@ -145,6 +146,10 @@ def main():
     ap.add_argument("--mask", choices=["none", "rows", "heads"], default="none",
                     help="run paged_extend_attn_masked with an all-keep mask of [B, 1, max_q_len, Ks] (rows) or "
                          "[B, Hq, max_q_len, Ks] (heads): same visible pairs, so the TFLOP/s show the mask's cost")
+    ap.add_argument("--append", choices=["separate", "fused"], default="fused",
+                    help="fused (default): paged_extend_attn_append, whose bf16 attention launch also writes the "
+                         "chunk's K/V into the pool when the plan's slot_blocks <= 128 (else it runs the append "
+                         "kernel first); separate: pkv_append then paged_extend_attn")
     ap.add_argument("--rope", action="store_true",
                     help="the step rotates q and k at their absolute positions with pkv_rope_append (in place "
                          "of pkv_append) before the attention; reports that kernel's HBM rate")
@@ -246,6 +251,12 @@ def main():
                               cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, vp(b["mask"]), mh,
                               int(L.max()), ks, ctypes.byref(plan), ctypes.byref(shape), vp(out), vp(ws), ws.numel(),
                               sh)
+        if args.append == "fused":
+            b["append_fn"] = None
+            b["attn_fn"] = lib.paged_extend_attn_append
+            b["attn_args"] = (vp(q), vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
+                              cache.page_table.shape[1], None, bw.window, 0.0, ctypes.byref(plan),
+                              ctypes.byref(shape), vp(out), vp(ws), ws.numel(), sh)
         B.append(b)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -258,7 +269,7 @@ def main():
         for i, b in enumerate(B):
             if build(*b["meta_args"][s]):
                 raise RuntimeError(lib.pkv_last_error().decode())
-            if b["append_fn"](*b["append_args"]):
+            if b["append_fn"] is not None and b["append_fn"](*b["append_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
             k = 2 * (s * len(B) + i)
             if bracket:
@@ -295,7 +306,7 @@ def main():
     e0.record(stream)
     for _ in range(args.steps):
         for b in B:
-            if b["append_fn"](*b["append_args"]):
+            if b["append_fn"] is not None and b["append_fn"](*b["append_args"]):
                 raise RuntimeError(lib.pkv_last_error().decode())
     e1.record(stream)
     torch.cuda.synchronize()
@@ -309,9 +320,14 @@ def main():
     attn_tflops = flops / (attn_total_ms * 1e-3) / 1e12
     attn_gbs = hbm_bytes / (attn_total_ms * 1e-3) / 1e9
     n_launch = len(B)
+    # launches whose append ran inside the attention kernel (paged_extend_attn_append's choice)
+    n_fused = sum(1 for b in B if args.append == "fused" and w.dtype == "bf16" and b["plan"].total_q > 0 and
+                  b["plan"].slot_blocks <= FUSE_MAX_SLOT_BLOCKS)
     decode_bound = args.workload == "decode64"
     roofline = {
-        "kernel": f"extend_attn_{w.dtype}<{w.head_dim}>" + (" + combine_splits" if any(
+        "kernel": f"extend_attn_{w.dtype}<{w.head_dim}>" + (
+                  f" (append fused in {n_fused} of {n_launch} launches)" if n_fused else "") +
+                  (" + combine_splits" if any(
             b["plan"].n_split_rows for b in B) else ""),
         "bound": "hbm" if decode_bound else "mfma",
         "achieved": round(attn_gbs if decode_bound else attn_tflops, 3),
@@ -350,7 +366,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
         "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope),
-                   "explicit_mask": args.mask, "batches_per_step": len(B),
+                   "explicit_mask": args.mask, "append": args.append, "batches_per_step": len(B),
                    "query_tokens_per_step": tokens, "flops_per_step": flops},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
@@ -362,10 +378,12 @@ def main():
     rope_cpu = None
     if args.rope and not args.no_cpu_baseline:
         rope_cpu = cpu_rope_baseline(batches, w, rope_table.cpu().numpy())
-    line["append"] = {"kernel": "pkv_rope_append (rotary q, k + append)" if args.rope else "pkv_append",
+    line["append"] = {"kernel": "pkv_rope_append (rotary q, k + append)" if args.rope else
+                      (f"paged_extend_attn_append: inside the attention launch in {n_fused} of {n_launch} "
+                       "calls, the append kernel first in the others" if args.append == "fused" else "pkv_append"),
                       "ms_per_step": round(append_ms, 4), "bytes_per_step": append_bytes,
-                      "gbs_algorithmic": round(append_bytes / (append_ms * 1e-3) / 1e9, 1) if append_ms > 0 else None,
-                      "hbm_frac": round(append_bytes / (append_ms * 1e-3) / 1e9 / HBM_PEAK, 4) if append_ms > 0 else None}
+                      "gbs_algorithmic": round(append_bytes / (append_ms * 1e-3) / 1e9, 1) if append_ms > 0.01 else None,
+                      "hbm_frac": round(append_bytes / (append_ms * 1e-3) / 1e9 / HBM_PEAK, 4) if append_ms > 0.01 else None}
     if rope_cpu is not None:
         line["append"]["cpu_baseline"] = rope_cpu
     if graph_replay is not None:
@@ -387,13 +405,14 @@ def time_graph_replay(args, B, lib, flops, tokens):
         ap = b["append_args"][:-1] + (sh,)
         at = b["attn_args"][:-1] + (sh,)
         torch.cuda.synchronize()
+        app = (lambda: b["append_fn"](*ap)) if b["append_fn"] is not None else (lambda: 0)
         with torch.cuda.stream(s):       # one eager pass on the capture stream first
-            if b["append_fn"](*ap) or b["attn_fn"](*at):
+            if app() or b["attn_fn"](*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            if b["append_fn"](*ap) or b["attn_fn"](*at):
+            if app() or b["attn_fn"](*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
         graphs.append(g)
     for _ in range(args.warmup):

@@ -100,6 +100,8 @@ typedef struct pkv_plan {
   int32_t max_splits;     /* split stride of the partial buffers                */
   int32_t window;         /* sliding window W (<= 0: none)                      */
   int32_t flags;          /* PKV_FLAG_* the plan was built with                 */
+  int32_t slot_blocks;    /* estimated 64-key blocks of the busiest workgroup   */
+                          /* slot: max(longest item, all items / slots)        */
   pkv_shape shape;        /* the shape the plan was built for                   */
   size_t workspace_bytes; /* scratch paged_extend_attn needs (0 if no splits)   */
   /* device pointers (NULL after a host-only build) */
@@ -281,11 +283,13 @@ int paged_extend_attn_masked(const void* q, const void* k_pool, const void* v_po
  * written to the slots of positions start_pos .. seq_len-1, then the paged
  * attention reads the cache). Output and every pool byte equal those of
  * pkv_append followed by paged_extend_attn, bit for bit.
- * bf16: a single attention launch does both. Its gather reads key positions
- * >= P_b from k_new / v_new rather than from the pool, and each new row is
- * copied into its slot by the one work item whose query tile holds that token
- * and whose key range holds its position (split-row combine as usual).
- * fp32: the append kernel runs first, then the attention.
+ * bf16, when the plan's slot_blocks is at most 128: a single attention launch
+ * does both. Its gather reads key positions >= P_b from k_new / v_new rather
+ * than from the pool, and each new row is copied into its slot by the one work
+ * item whose query tile holds that token and whose key range holds its
+ * position (split-row combine as usual). Otherwise (longer launches, where the
+ * fused gather's per-lane addressing costs more than the launch it saves) and
+ * for fp32: the append kernel runs first, then the attention.
  *   k_new, v_new   [total_q, Hkv, D]; must not overlap the pools
  *   k_pool, v_pool read at positions < P_b, written at P_b .. N_b - 1
  * The batch offsets are the plan's (qo_indptr, kv_indptr, prefix_lens).

@@ -34,6 +34,7 @@ class PkvPlan(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("total_q", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
                 ("max_kv_len", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_split_rows", ctypes.c_int32),
                 ("max_splits", ctypes.c_int32), ("window", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("slot_blocks", ctypes.c_int32),
                 ("shape", PkvShape),
                 ("workspace_bytes", ctypes.c_size_t),
                 ("qo_indptr", ctypes.c_void_p), ("kv_indptr", ctypes.c_void_p),

@@ -350,7 +350,7 @@ int paged_extend_attn_append(const void* q, const void* k_new, const void* v_new
         if (overlap(n, new_bytes, pl, pool_bytes))
           return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: k_new / v_new overlap a pool", name);
   }
-  if (shape->dtype != PKV_DTYPE_BF16) {
+  if (shape->dtype != PKV_DTYPE_BF16 || plan->slot_blocks > kFuseMaxSlotBlocks) {
     if ((st = pkv_append(k_new, v_new, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, plan, shape,
                          stream)))
       return st;

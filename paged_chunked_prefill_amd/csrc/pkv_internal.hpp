@@ -27,6 +27,11 @@ constexpr int kTileKeysF32 = 32;
 // Every split of a one-token row covers whole 64-key blocks, so the tile
 // boundaries of both instantiations stay aligned to absolute positions.
 constexpr int kSplitGranule = 64;
+// paged_extend_attn_append fuses the append into the bf16 attention launch
+// while the plan's busiest workgroup slot streams at most this many 64-key
+// blocks: the fused gather's per-lane addresses cost a little per block, the
+// separate append launch a fixed few microseconds.
+constexpr int kFuseMaxSlotBlocks = 128;
 // Cap on the KV splits of one prefill tile.
 constexpr int kMaxPrefillSplits = 16;
 // Compute units of an MI355X; the planner sizes splits for this machine.

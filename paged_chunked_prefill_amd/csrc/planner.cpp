@@ -299,6 +299,15 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   const int32_t n_items = int32_t(items.size());
   const MetaLayout lay = meta_layout(batch, n_items, n_split_rows);
   if (meta_bytes_out) *meta_bytes_out = lay.total;
+  // key blocks the busiest workgroup slot streams: the longest item, or the
+  // average per slot when there are more items than slots
+  int64_t max_blocks = 0, sum_blocks = 0;
+  for (const WorkItem& it : items) {
+    const int64_t nb = it.kv_end > it.kv_begin ? ceil_div(it.kv_end, kSplitGranule) - it.kv_begin / kSplitGranule : 0;
+    max_blocks = std::max(max_blocks, nb);
+    sum_blocks += nb;
+  }
+  const int64_t slot_blocks = std::max(max_blocks, (sum_blocks + slots - 1) / slots);
 
   if (plan) {
     std::memset(plan, 0, sizeof(*plan));
@@ -311,6 +320,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     plan->max_splits = max_splits;
     plan->window = window;
     plan->flags = flags;
+    plan->slot_blocks = int32_t(std::min<int64_t>(slot_blocks, INT32_MAX));
     plan->shape = *shape;
     plan->workspace_bytes = workspace_bytes(n_split_rows, hq, max_splits, shape->head_dim, shape->dtype);
   }

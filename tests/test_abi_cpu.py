@@ -291,6 +291,23 @@ def test_auto_splits_follow_the_cu_heuristic():
     assert p.plan.max_splits == 1
 
 
+def test_slot_blocks_estimate():
+    """plan.slot_blocks (the fused-append choice): the 64-key blocks of the
+    longest item, or of the average slot when items outnumber the 256 slots."""
+    cases = [([3584], [512], shape(16, 4, 128, 64, 1000)),
+             ([16384, 16384], [2048, 2048], shape(64, 8, 128, 16, 5000)),
+             ([100, 0, 7], [1, 300, 65], shape(32, 8, 128, 16, 100)),
+             ([6000] * 8, [1000] * 8, shape(32, 8, 128, 16, 4000))]
+    for P, L, s in cases:
+        p = pkv.build_extend_metadata(P, L, s, 4096 if P[0] == 6000 else 0)
+        blocks = [-(-int(x["kv_end"]) // 64) - int(x["kv_begin"]) // 64 if x["kv_end"] > x["kv_begin"] else 0
+                  for x in p.host_sections()["items"]]
+        assert p.plan.slot_blocks == max(max(blocks), -(-sum(blocks) // 256)), (P, L)
+    # the headline chunk is fused, the long prefills are not
+    assert pkv.build_extend_metadata([3584], [512], cases[0][2]).plan.slot_blocks <= 128
+    assert pkv.build_extend_metadata([16384] * 2, [2048] * 2, cases[1][2]).plan.slot_blocks > 128
+
+
 def test_prefill_tiles_split_only_when_few():
     """A launch with fewer items than 2 per compute unit cuts its longest tiles
     over KV (whole 64-key blocks, >= 2 per split); a full launch is not cut."""

@@ -136,6 +136,17 @@ def test_fused_random(data):
     check_oracle(f"random {dtype} D={D} {hq}/{hkv} ps={ps} W={window} S={splits} P={P} L={L}", out, w)
 
 
+def test_long_launch_takes_the_append_kernel():
+    """A plan whose busiest slot streams more than 128 key blocks (16 requests
+    of 8000 cached + 256 new tokens: 512 items of about 130 blocks): the call
+    runs the append kernel and the plain attention, with the same bits as the
+    two calls."""
+    w = small("bf16", [8000] * 16, [256] * 16, 32, 8, 128, 64, seed=11)
+    plan = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape_of(w), 0, 0, device="cuda")
+    assert plan.plan.slot_blocks > 128
+    fused_and_two_call(w)
+
+
 def test_fused_bad_page_is_flagged_and_not_written():
     """A new position whose page id lies outside the pool: the status word says
     so and no pool byte is written for it (the two-call path skips it too)."""

@@ -35,11 +35,13 @@ def _workload(name):
     return wl.config4(mid_page=True)   # window, no splits
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_append"])
 @pytest.mark.parametrize("name", ["ragged_splits", "decode_splits", "window"])
-def test_graph_replay_matches_eager(name):
+def test_graph_replay_matches_eager(name, fused):
     w = _workload(name)
     dev = torch.device("cuda", torch.cuda.current_device())
-    print(f"[graph] {name}: P={list(w.prefix_lens)[:4]} L={list(w.chunk_lens)[:4]} batch={w.batch}", flush=True)
+    print(f"[graph] {name} fused={fused}: P={list(w.prefix_lens)[:4]} L={list(w.chunk_lens)[:4]} batch={w.batch}",
+          flush=True)
     cache = DeviceCache(w, dev)
     cache.fill_prefix(w)
     plan = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape_of(w), w.window, w.decode_splits, device=dev)
@@ -49,6 +51,10 @@ def test_graph_replay_matches_eager(name):
     ws = plan.workspace()   # allocated before capture
 
     def path():
+        if fused:   # paged_extend_attn_append: one launch for these plans where it fuses
+            pkv.paged_extend_attn_append(q, kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out,
+                                         workspace=ws)
+            return
         pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan)
         pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out, workspace=ws)
 
