@@ -199,6 +199,8 @@ def main():
     max_pos = max(int((np.asarray(bw.prefix_lens) + np.asarray(bw.chunk_lens)).max()) for bw in batches)
     rope_table = torch.from_numpy(wl.rope_table(max_pos + 1, w.head_dim)).to(dev) if args.rope else None
     esize = 2 if w.dtype == "bf16" else 4
+    # the rotary append and the masked attention keep their own calls
+    fuse_mode = args.append == "fused" and not args.rope and args.mask == "none"
     # per batch: device inputs, output, metadata buffers, pre-marshalled ctypes arguments
     B = []
     for bw in batches:
@@ -251,7 +253,7 @@ def main():
                               cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, vp(b["mask"]), mh,
                               int(L.max()), ks, ctypes.byref(plan), ctypes.byref(shape), vp(out), vp(ws), ws.numel(),
                               sh)
-        if args.append == "fused":
+        if fuse_mode:
             b["append_fn"] = None
             b["attn_fn"] = lib.paged_extend_attn_append
             b["attn_args"] = (vp(q), vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
@@ -321,7 +323,7 @@ def main():
     attn_gbs = hbm_bytes / (attn_total_ms * 1e-3) / 1e9
     n_launch = len(B)
     # launches whose append ran inside the attention kernel (paged_extend_attn_append's choice)
-    n_fused = sum(1 for b in B if args.append == "fused" and w.dtype == "bf16" and b["plan"].total_q > 0 and
+    n_fused = sum(1 for b in B if fuse_mode and w.dtype == "bf16" and b["plan"].total_q > 0 and
                   b["plan"].slot_blocks <= FUSE_MAX_SLOT_BLOCKS)
     decode_bound = args.workload == "decode64"
     roofline = {
@@ -344,8 +346,10 @@ def main():
     if tr is not None:
         # HBM bytes per attention kernel launch from the FETCH_SIZE / WRITE_SIZE counters, scaled by the
         # same counters on a copy of known size; the split combine's bytes are not in it
+        # a launch with the append fused in also reads the chunk's K/V rows and writes them into the pool
+        alg = hbm_bytes + (append_bytes if n_fused == n_launch else 0)
         roofline["traffic"] = tr["traffic_bytes_per_launch"]
-        roofline["traffic_vs_algorithmic_bytes"] = round(tr["traffic_bytes_per_launch"] / (hbm_bytes / n_launch), 3)
+        roofline["traffic_vs_algorithmic_bytes"] = round(tr["traffic_bytes_per_launch"] / (alg / n_launch), 3)
         roofline["traffic_source"] = f"profiles/traffic_{args.workload}.json"
 
     graph_replay = None
@@ -366,7 +370,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
         "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope),
-                   "explicit_mask": args.mask, "append": args.append, "batches_per_step": len(B),
+                   "explicit_mask": args.mask, "append": "fused" if fuse_mode else "separate",
+                   "batches_per_step": len(B),
                    "query_tokens_per_step": tokens, "flops_per_step": flops},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
@@ -380,7 +385,7 @@ def main():
         rope_cpu = cpu_rope_baseline(batches, w, rope_table.cpu().numpy())
     line["append"] = {"kernel": "pkv_rope_append (rotary q, k + append)" if args.rope else
                       (f"paged_extend_attn_append: inside the attention launch in {n_fused} of {n_launch} "
-                       "calls, the append kernel first in the others" if args.append == "fused" else "pkv_append"),
+                       "calls, the append kernel first in the others" if fuse_mode else "pkv_append"),
                       "ms_per_step": round(append_ms, 4), "bytes_per_step": append_bytes,
                       "gbs_algorithmic": round(append_bytes / (append_ms * 1e-3) / 1e9, 1) if append_ms > 0.01 else None,
                       "hbm_frac": round(append_bytes / (append_ms * 1e-3) / 1e9 / HBM_PEAK, 4) if append_ms > 0.01 else None}
