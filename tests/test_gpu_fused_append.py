@@ -84,6 +84,11 @@ def small(dtype, P, L, hq, hkv, D, ps, window=0, seed=3, splits=0):
     ("bf16", [2047, 3000, 17], [1, 1, 1], 64, 8, 128, 16, 0, 8),   # one-token rows, 8 splits
     ("bf16", [800, 5, 0], [1, 0, 129], 16, 4, 128, 64, 0, 0),      # an empty chunk between rows
     ("fp32", [20, 47], [45, 33], 4, 2, 64, 16, 0, 0),     # fp32: the append kernel then the attention
+    # every prefix a multiple of 8: no 4- or 8-row gather copy straddles P_b
+    ("bf16", [0, 512, 1024], [64, 128, 512], 32, 8, 128, 16, 0, 0),
+    ("bf16", [64, 8, 0], [100, 1, 77], 8, 2, 64, 64, 0, 3),
+    ("bf16", [4096, 16], [300, 40], 16, 4, 128, 16, 1000, 0),
+    ("bf16", [0], [700], 4, 4, 128, 64, 0, 0),            # aligned, G=1: owned rows past the prologue's
 ])
 def test_fused_matches_two_calls_and_oracle(dtype, P, L, hq, hkv, D, ps, window, splits):
     w = small(dtype, P, L, hq, hkv, D, ps, window, splits=splits)
@@ -122,6 +127,8 @@ def test_fused_random(data):
     D = data.draw(st.sampled_from([64, 128]))
     B = data.draw(st.integers(1, 4))
     P = data.draw(st.lists(st.integers(0, 700), min_size=B, max_size=B))
+    if data.draw(st.booleans()):
+        P = [8 * (x // 8) for x in P]     # aligned prefixes: no gather copy straddles P_b
     L = data.draw(st.lists(st.sampled_from([0, 1, 1, 3, 16, 33, 64, 100, 257]), min_size=B, max_size=B))
     if sum(L) == 0:
         L[0] = 1
