@@ -137,7 +137,7 @@ class ExtendPlan:
         raw_items, items = out["items"], np.zeros(ni, WORK_ITEM_VIEW)
         for f in WORK_ITEM_DTYPE.names:
             items[f] = raw_items[f]
-        items["kv_head"] = raw_items["head_split"] >> SPLIT_BITS
+        items["kv_head"] = raw_items["head_split"] >> (2 * SPLIT_BITS)
         items["split"] = raw_items["head_split"] & ((1 << SPLIT_BITS) - 1)
         items["q_begin"] = raw_items["tok0"] - out["qo_indptr"][raw_items["req"]]
         out["items"] = items

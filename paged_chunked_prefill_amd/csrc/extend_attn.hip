@@ -113,7 +113,7 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Per-item geometry shared by both instantiations.
 struct ItemView {
-  int req, kv_head, split, q_count, kv_begin, kv_end, part_row;
+  int req, kv_head, split, nsplit, q_count, kv_begin, kv_end, part_row;
   int tok0, pos0, pt_row;
 };
 
@@ -121,8 +121,9 @@ __device__ inline ItemView load_item(const Params& p) {
   const WorkItem it = p.items[blockIdx.x];
   ItemView v;
   v.req = it.req;
-  v.kv_head = it.head_split >> kSplitBits;
+  v.kv_head = it.head_split >> (2 * kSplitBits);
   v.split = it.head_split & ((1 << kSplitBits) - 1);
+  v.nsplit = max(1, (it.head_split >> kSplitBits) & ((1 << kSplitBits) - 1));
   v.part_row = it.part_row;
   v.tok0 = it.tok0;
   v.pos0 = it.pos0;
@@ -469,31 +470,29 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
     for (int k = 0; k < kMaskWords; ++k) asm volatile("" : "+v"(w[k]));
   };
 
-  // Fused append: this item owns the new rows of its KV head at the positions of
-  // its own tokens that fall in its key range (each new row lies in exactly one
-  // split of the tile holding its token). The first OWN_TOK of them are loaded
-  // with tile 0 (loads the compiler does not see, so the prologue's wait covers
-  // them without waiting for tiles 1-2) and stored after that wait; any rest
-  // (more than OWN_TOK tokens per tile: G < 4 at D = 128) after the tile loop.
-  // Lane vector v: token v / (2 VPR), K for the first VPR vectors, then V.
+  // Fused append: the S splits of a tile share the copying of its tokens' new
+  // rows (KV head of the item): split k takes tokens t = k, k + S, k + 2S, ...
+  // (every row once, whatever the key ranges). The first OWN_VECS vectors are
+  // loaded with tile 0 (loads the compiler does not see, so the prologue's
+  // wait covers them without waiting for tiles 1-2) and stored after that
+  // wait; any rest (more than 64 owned tokens at D = 128) after the tile loop.
+  // Lane vector v: owned token v / (2 VPR), K for the first VPR vectors, then V.
   constexpr int VPR = D * 2 / 16;                        // 16-byte vectors of one head's row
   constexpr int NOWN = 4;                                // vectors per lane in the prologue copy
   constexpr int OWN_VECS = 64 * kWavesBf16 * NOWN;
-  int own_lo = 0, own_n = 0;
-  if constexpr (FUSED) {
-    own_lo = max(it.kv_begin, tile_pos);
-    own_n = max(0, min(it.kv_end, tile_pos + it.q_count) - own_lo);
-  }
+  int own_n = 0;   // tokens this item copies
+  if constexpr (FUSED)
+    own_n = it.split < it.q_count ? (it.q_count - it.split + it.nsplit - 1) / it.nsplit : 0;
   struct OwnVec {
     const char* src;
     char* dst;    // pool slot, page not yet applied
     int col;      // page-table column of the row
   };
   auto own_vec = [&](int v) __attribute__((always_inline)) {
-    const int t = v / (2 * VPR), rem = v - t * (2 * VPR);
+    const int u = v / (2 * VPR), rem = v - u * (2 * VPR);
     const bool isv = rem >= VPR;
     const int e = isv ? rem - VPR : rem;
-    const int pos = own_lo + t;
+    const int pos = tile_pos + it.split + u * it.nsplit;
     const int64_t head_off = int64_t(it.kv_head) * D * 2 + 16 * e;
     OwnVec o;
     o.src = (isv ? vnew : knew) + int64_t(pos - fresh0) * row_bytes + head_off;
@@ -747,7 +746,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // no copy into LDS outlives the workgroup
   if constexpr (FUSED) {
     // owned rows past the prologue's share (plain loads and stores)
-    for (int v = tid + OWN_VECS; v < own_n * 2 * VPR; v += 64 * kWavesBf16) {
+    for (int v = tid + (ntiles > 0 ? OWN_VECS : 0); v < own_n * 2 * VPR; v += 64 * kWavesBf16) {
       const OwnVec o = own_vec(v);
       const int page = pt[o.col];
       const bool ok = uint32_t(page) < uint32_t(p.num_pages);

@@ -46,7 +46,7 @@ constexpr int kXcds = 8;
 // starts from this one 32-byte record.
 struct alignas(16) WorkItem {
   int32_t req;         // request index b (page-table row, or index into req_pool_indices)
-  int32_t head_split;  // KV head hk << 8 | split index within the tile's row (0 when unsplit)
+  int32_t head_split;  // KV head hk << 16 | the tile's split count S << 8 | split index k (S = 1, k = 0 unsplit)
   int32_t tok0;        // global token index of the tile's first token: qo_indptr[b] + first chunk token
   int32_t pos0;        // its absolute position: P_b + first chunk token
   int32_t q_count;     // tokens in the tile (>= 1, all inside the chunk)
@@ -55,7 +55,7 @@ struct alignas(16) WorkItem {
   int32_t part_row;    // -1: write `out`; else partial slot of the tile's first token
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
-constexpr int kSplitBits = 8;
+constexpr int kSplitBits = 8;   // width of the split index and of the split count in head_split
 // Non-causal plans put an item's pos0 (the position its causal bound is taken
 // from) past every key, so the kernels' causal test passes for all of them.
 constexpr int32_t kNonCausalPos = 1 << 30;  // split index field of head_split (splits <= PKV_MAX_SPLITS < 256)

@@ -81,8 +81,11 @@ std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
   }
   // locality groups: items with equal (request, KV head, split)
   std::vector<std::pair<uint64_t, uint32_t>> keyed(n);
-  for (size_t i = 0; i < n; ++i)
-    keyed[i] = {(uint64_t(uint32_t(in[i].req)) << 32) | uint64_t(uint32_t(in[i].head_split)), uint32_t(i)};
+  for (size_t i = 0; i < n; ++i) {
+    // (the split count bits stay out of the key: the groups are as before)
+    const uint32_t hk = uint32_t(in[i].head_split) >> (2 * kSplitBits), k = uint32_t(in[i].head_split) & 0xffu;
+    keyed[i] = {(uint64_t(uint32_t(in[i].req)) << 32) | (uint64_t(hk) << kSplitBits) | k, uint32_t(i)};
+  }
   std::sort(keyed.begin(), keyed.end());
   std::vector<uint32_t> group_of(n);
   std::vector<int64_t> group_cost;
@@ -259,7 +262,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       for (int32_t k = 0; k < splits; ++k) {
         WorkItem it;
         it.req = t.req;
-        it.head_split = (h << kSplitBits) | k;
+        it.head_split = (h << (2 * kSplitBits)) | (splits << kSplitBits) | k;
         it.tok0 = qo_start[t.req] + t.q_begin;
         it.pos0 = causal ? prefix_lens[t.req] + t.q_begin : kNonCausalPos;
         it.q_count = t.q_count;
