@@ -285,9 +285,10 @@ int paged_extend_attn_masked(const void* q, const void* k_pool, const void* v_po
  * pkv_append followed by paged_extend_attn, bit for bit.
  * bf16, when the plan's slot_blocks is at most 128: a single attention launch
  * does both. Its gather reads key positions >= P_b from k_new / v_new rather
- * than from the pool, and each new row is copied into its slot by the one work
- * item whose query tile holds that token and whose key range holds its
- * position (split-row combine as usual). Otherwise (longer launches, where the
+ * than from the pool, and each new row is copied into its slot by one work
+ * item of the query tile holding that token (of a tile cut into S key
+ * splits, split k copies the tile's tokens k, k + S, ...; split-row combine
+ * as usual). Otherwise (longer launches, where the
  * fused gather's per-lane addressing costs more than the launch it saves) and
  * for fp32: the append kernel runs first, then the attention.
  *   k_new, v_new   [total_q, Hkv, D]; must not overlap the pools
