@@ -554,11 +554,7 @@ def cpu_baseline(w, batches, sample_rows):
     from pkv_testlib import oracle_pools
     import workloads as wl
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    cores, blas = blas_info()
     last = batches[-1]
     if len(batches) > 1 and last.batch == 1:    # chunked prompt: the whole prompt as one full prefill
         full = last.with_lengths([0], [int(last.kv_lens[0])])
@@ -597,8 +593,24 @@ def cpu_baseline(w, batches, sample_rows):
         vis = pos + 1 if sub.window <= 0 else min(pos + 1, sub.window)
         flops += 4 * sub.head_dim * sub.num_q_heads * vis
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3), "tokens_per_s": round(len(sub_rows) / dt, 2),
+            "seconds": round(dt, 3), "tokens_per_s": round(len(sub_rows) / dt, 2), "blas": blas,
             "sample": f"{len(sub_rows)} of {rows_total} query rows (all heads), fp32 NumPy oracle"}
+
+
+def blas_info():
+    """(threads the BLAS runs with, its vendor / version / threading as one string)."""
+    import numpy  # noqa: F401  (loads the BLAS that threadpoolctl then reports)
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # noqa: BLE001
+        libs = []
+    if not libs:
+        return len(os.sched_getaffinity(0)), "unknown"
+    b = libs[0]
+    desc = (f"{b.get('internal_api', '?')} {b.get('version', '?')} ({b.get('threading_layer', '?')}, "
+            f"{b.get('num_threads', '?')} threads, {b.get('architecture', '?')} kernels)")
+    return int(b.get("num_threads", 1)), desc
 
 
 if __name__ == "__main__":

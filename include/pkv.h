@@ -80,7 +80,7 @@ enum { PKV_FLAG_NON_CAUSAL = 1 };
 /* Geometry of one attention layer's cache. */
 typedef struct pkv_shape {
   int32_t num_q_heads;  /* Hq                                                   */
-  int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 128              */
+  int32_t num_kv_heads; /* Hkv < 32768; Hq % Hkv == 0, G = Hq / Hkv <= 128      */
   int32_t head_dim;     /* D in {64, 128}                                       */
   int32_t page_size;    /* ps >= 1 tokens per page                              */
   int32_t num_pages;    /* pages in each pool                                   */
@@ -102,6 +102,7 @@ typedef struct pkv_plan {
   int32_t flags;          /* PKV_FLAG_* the plan was built with                 */
   int32_t slot_blocks;    /* estimated 64-key blocks of the busiest workgroup   */
                           /* slot: max(longest item, all items / slots)        */
+  int32_t num_cus;        /* compute units the work list was sized for          */
   pkv_shape shape;        /* the shape the plan was built for                   */
   size_t workspace_bytes; /* scratch paged_extend_attn needs (0 if no splits)   */
   /* device pointers (NULL after a host-only build) */
@@ -114,7 +115,9 @@ typedef struct pkv_plan {
 } pkv_plan;
 
 /*
- * Size query for build_extend_metadata's buffers (host only, no GPU use).
+ * Size query for build_extend_metadata's buffers (host only: no device work;
+ * the compute-unit count of the current HIP device is read as
+ * build_extend_metadata reads it, so that both calls plan the same work list).
  *   prefix_lens_h, chunk_lens_h  host int32 [batch]: P_b >= 0, L_b >= 0
  *   window                       W (<= 0: none)
  *   decode_splits                KV splits for one-token chunks; 0 = choose
@@ -135,7 +138,12 @@ int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const 
  * Computes qo_indptr (exclusive cumsum of L_b), kv_indptr (exclusive cumsum
  * of N_b = P_b + L_b), a copy of prefix_lens and the attention work list into
  * meta_host, then enqueues one host-to-device copy of meta_host into meta_dev
- * on `stream`. No device synchronisation.
+ * on `stream`. No device synchronisation. The work list is sized for the
+ * compute units of the current HIP device (AstrAI compare, csrc/kernels/
+ * attn_dispatchers.cuh: get_sm_count caches the count per device and
+ * compute_num_splits sizes the KV splits from it): its count is read once per
+ * device and cached; with no current device (a host-only plan on a machine
+ * without a GPU) the plan is sized for an MI355X's 256.
  *   meta_host   caller buffer of >= meta_bytes; it must stay unchanged until
  *               the copy has executed (pinned memory makes the copy async).
  *   meta_dev    device buffer of >= meta_bytes, or NULL for a host-only plan
@@ -145,9 +153,10 @@ int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const 
  * Errors: PKV_ERR_INVALID_ARGUMENT (null pointers, batch < 1, negative
  * lengths, int32 overflow of the sums, Hq % Hkv != 0, page_size < 1,
  * num_pages < 1, decode_splits outside 0..PKV_MAX_SPLITS),
- * PKV_ERR_UNSUPPORTED (head_dim not 64/128, dtype unknown, G > 128, one
- * token row of a pool >= 2^24 bytes or one page > 2^31-1 bytes, device not
- * gfx950), PKV_ERR_WORKSPACE (a buffer too small), PKV_ERR_HIP.
+ * PKV_ERR_UNSUPPORTED (head_dim not 64/128, dtype unknown, G > 128,
+ * Hkv >= 32768, one token row of a pool >= 2^24 bytes or one page > 2^31-1
+ * bytes, device not gfx950), PKV_ERR_WORKSPACE (a buffer too small),
+ * PKV_ERR_HIP.
  */
 int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                           const pkv_shape* shape, int32_t window, int32_t decode_splits,
@@ -156,19 +165,24 @@ int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int
 
 /*
  * build_extend_metadata_ex, pkv_extend_metadata_size_ex -- the same with
- * `flags` (PKV_FLAG_*; 0 is build_extend_metadata). With PKV_FLAG_NON_CAUSAL
- * each tile's key range is its request's whole [0, N_b) and the attention
- * applies no causal bound; pkv_append and paged_extend_attn take the plan
- * unchanged. Errors as build_extend_metadata, plus PKV_ERR_INVALID_ARGUMENT
- * for unknown flags or a window with PKV_FLAG_NON_CAUSAL.
+ * `flags` and `num_cus` (flags 0 and num_cus 0 are build_extend_metadata).
+ *   flags    PKV_FLAG_*. With PKV_FLAG_NON_CAUSAL each tile's key range is its
+ *            request's whole [0, N_b) and the attention applies no causal
+ *            bound; pkv_append and paged_extend_attn take the plan unchanged.
+ *   num_cus  compute units to size the work list for (the KV splits fill
+ *            num_cus resident workgroup slots); 0 = the current device's
+ *            count as above. A plan sized for more units than the device has
+ *            is still correct, only slower. At most 65536.
+ * Errors as build_extend_metadata, plus PKV_ERR_INVALID_ARGUMENT for unknown
+ * flags, a window with PKV_FLAG_NON_CAUSAL, or num_cus outside 0..65536.
  */
 int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                              const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
-                             void* meta_host, size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes,
-                             pkv_plan* plan_out, pkv_stream_t stream);
+                             int32_t num_cus, void* meta_host, size_t meta_host_bytes, void* meta_dev,
+                             size_t meta_dev_bytes, pkv_plan* plan_out, pkv_stream_t stream);
 int pkv_extend_metadata_size_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                                 const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
-                                size_t* meta_bytes, size_t* workspace_bytes);
+                                int32_t num_cus, size_t* meta_bytes, size_t* workspace_bytes);
 
 /*
  * pkv_append -- step a2: write the chunk's new K/V into the pools
@@ -180,7 +194,9 @@ int pkv_extend_metadata_size_ex(int32_t batch, const int32_t* prefix_lens_h, con
  * qo_indptr[b]+i into slot (page_table[row_b][p / page_size], p % page_size)
  * of k_pool/v_pool. Bit copy; no other pool byte is written.
  *   page_table_stride   entries per page-table row; must cover max_kv_len
- *   req_pool_indices    device int32 [batch] or NULL (row b = b)
+ *   req_pool_indices    device int32 [batch] or NULL (row b = b); every
+ *                       value must be a row of page_table (device data: not
+ *                       checked, like the data pointers themselves)
  * Errors: PKV_ERR_INVALID_ARGUMENT (null pointer, plan/shape mismatch, stride
  * too small), PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
  */
@@ -230,9 +246,14 @@ int pkv_rope_append(const void* q, void* q_out, const void* k_new, const void* v
  * Row i of request b, query head h, sees key positions j with
  *   j <= P_b + i   and   (window <= 0 or j >= P_b + i - window + 1)
  * and gets softmax(sm_scale * q.k_j) weighted V of those keys (0 if none).
- *   qo_indptr, kv_indptr, prefix_lens   device int32 arrays ([B+1],[B+1],[B]);
- *        NULL takes the plan's copies. They must describe the same batch as
- *        the plan (kv_indptr[b+1]-kv_indptr[b] == prefix_lens[b] + L_b).
+ *   qo_indptr, kv_indptr, prefix_lens   device int32 arrays ([B+1],[B+1],[B])
+ *        describing the batch: each must be NULL or the plan's own device
+ *        array (plan->qo_indptr, ...), which hold exactly these prefix sums
+ *        and lengths (so prefix_lens[b] == kv_indptr[b+1] - kv_indptr[b] -
+ *        (qo_indptr[b+1] - qo_indptr[b]) always holds). Any other pointer is
+ *        rejected with PKV_ERR_INVALID_ARGUMENT: the work list carries every
+ *        offset, and device arrays of the caller cannot be compared with the
+ *        plan without a host synchronisation.
  *   window     must equal the plan's window.
  *   sm_scale   softmax scale; <= 0 selects 1/sqrt(head_dim).
  *   out        [total_q, Hq, D] written for every row.

@@ -83,17 +83,12 @@ WORK_ITEM_VIEW = np.dtype(WORK_ITEM_DTYPE.descr + [("kv_head", "<i4"), ("split",
 
 
 def extend_metadata_size(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0,
-                         causal: bool = True):
+                         causal: bool = True, num_cus: int = 0):
     P, L = _i32(prefix_lens), _i32(chunk_lens)
     mb, wb = ctypes.c_size_t(), ctypes.c_size_t()
-    if causal:
-        _check(_lib.pkv_extend_metadata_size(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                             int(decode_splits), ctypes.byref(mb), ctypes.byref(wb)),
-               "pkv_extend_metadata_size")
-    else:
-        _check(_lib.pkv_extend_metadata_size_ex(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                                PKV_FLAG_NON_CAUSAL, int(decode_splits), ctypes.byref(mb),
-                                                ctypes.byref(wb)), "pkv_extend_metadata_size_ex")
+    _check(_lib.pkv_extend_metadata_size_ex(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
+                                            0 if causal else PKV_FLAG_NON_CAUSAL, int(decode_splits), int(num_cus),
+                                            ctypes.byref(mb), ctypes.byref(wb)), "pkv_extend_metadata_size_ex")
     return mb.value, wb.value
 
 
@@ -152,31 +147,28 @@ def _stream_handle(stream, device):
 
 
 def build_extend_metadata(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0,
-                          device=None, stream=None, meta_host=None, meta_dev=None, causal: bool = True) -> ExtendPlan:
-    """Plan one step. ``device=None`` plans on the host only (no GPU call).
+                          device=None, stream=None, meta_host=None, meta_dev=None, causal: bool = True,
+                          num_cus: int = 0) -> ExtendPlan:
+    """Plan one step. ``device=None`` plans on the host only (no GPU work).
     ``meta_host`` (pinned uint8 tensor) and ``meta_dev`` (device uint8 tensor)
     may be given to reuse buffers; the host one must not be rewritten before
     the copy enqueued here has run. ``causal=False`` plans with
-    PKV_FLAG_NON_CAUSAL (build_extend_metadata_ex): every row sees its whole
-    request."""
+    PKV_FLAG_NON_CAUSAL: every row sees its whole request. ``num_cus`` sizes
+    the work list for that many compute units (0: the current device's)."""
     P, L = _i32(prefix_lens), _i32(chunk_lens)
     plan = PkvPlan()
 
     def call(host_ptr, host_bytes, dev_ptr, dev_bytes, st):
-        if causal:
-            return _check(_lib.build_extend_metadata(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                                     int(decode_splits), host_ptr, host_bytes, dev_ptr, dev_bytes,
-                                                     ctypes.byref(plan), st), "build_extend_metadata")
         return _check(_lib.build_extend_metadata_ex(len(L), _ptr(P), _ptr(L), ctypes.byref(shape), int(window),
-                                                    PKV_FLAG_NON_CAUSAL, int(decode_splits), host_ptr, host_bytes,
-                                                    dev_ptr, dev_bytes, ctypes.byref(plan), st),
-                      "build_extend_metadata_ex")
+                                                    0 if causal else PKV_FLAG_NON_CAUSAL, int(decode_splits),
+                                                    int(num_cus), host_ptr, host_bytes, dev_ptr, dev_bytes,
+                                                    ctypes.byref(plan), st), "build_extend_metadata_ex")
 
     if meta_host is not None and meta_dev is not None:
         call(ctypes.c_void_p(meta_host.data_ptr()), meta_host.numel(), ctypes.c_void_p(meta_dev.data_ptr()),
              meta_dev.numel(), _stream_handle(stream, meta_dev.device))
         return ExtendPlan(plan, shape, meta_host, meta_dev, P, L)
-    meta_bytes, _ = extend_metadata_size(P, L, shape, window, decode_splits, causal)
+    meta_bytes, _ = extend_metadata_size(P, L, shape, window, decode_splits, causal, num_cus)
     if device is None:
         host = np.zeros(meta_bytes, np.uint8)
         call(_ptr(host), meta_bytes, None, 0, None)
@@ -205,6 +197,10 @@ def _expect(t, shape, dtype, name):
 
 
 def _check_tables(page_table, plan: ExtendPlan, req_pool_indices):
+    """Types and shapes only: reading device values here would synchronise the
+    stream on every call (and could not be captured into a graph). The values
+    of req_pool_indices must be rows of page_table (check_req_pool_indices
+    checks a host copy)."""
     import torch
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
         raise ValueError("page_table must be a contiguous int32 [rows, stride] tensor")
@@ -212,11 +208,17 @@ def _check_tables(page_table, plan: ExtendPlan, req_pool_indices):
     if req_pool_indices is None:
         if rows < plan.plan.batch:
             raise ValueError("page_table has fewer rows than requests")
-    else:
-        if req_pool_indices.dtype != torch.int32 or req_pool_indices.numel() != plan.plan.batch:
-            raise ValueError("req_pool_indices must be int32 [batch]")
-        if int(req_pool_indices.min()) < 0 or int(req_pool_indices.max()) >= rows:
-            raise ValueError("req_pool_indices out of page_table rows")
+    elif req_pool_indices.dtype != torch.int32 or req_pool_indices.numel() != plan.plan.batch \
+            or not req_pool_indices.is_contiguous() or req_pool_indices.device != page_table.device:
+        raise ValueError("req_pool_indices must be a contiguous int32 [batch] tensor on the page table's device")
+
+
+def check_req_pool_indices(req_pool_indices_host, page_table_rows: int, batch: int) -> None:
+    """Host-side check of request-pool row indices before they are uploaded:
+    int32-representable, one per request, each a row of the page table."""
+    r = np.asarray(req_pool_indices_host)
+    if r.shape != (batch,) or r.size and (r.min() < 0 or r.max() >= page_table_rows):
+        raise ValueError(f"req_pool_indices must hold {batch} rows of a {page_table_rows}-row page table")
 
 
 def _pool_shape(s: PkvShape):

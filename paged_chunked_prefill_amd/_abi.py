@@ -34,7 +34,7 @@ class PkvPlan(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("total_q", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
                 ("max_kv_len", ctypes.c_int32), ("n_items", ctypes.c_int32), ("n_split_rows", ctypes.c_int32),
                 ("max_splits", ctypes.c_int32), ("window", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("slot_blocks", ctypes.c_int32),
+                ("slot_blocks", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("shape", PkvShape),
                 ("workspace_bytes", ctypes.c_size_t),
                 ("qo_indptr", ctypes.c_void_p), ("kv_indptr", ctypes.c_void_p),
@@ -64,10 +64,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
         "build_extend_metadata": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _P, _SZ, _P, _SZ,
                                   ctypes.POINTER(PkvPlan), _P],
-        "pkv_extend_metadata_size_ex": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _I32,
+        "pkv_extend_metadata_size_ex": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _I32, _I32,
                                         ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
-        "build_extend_metadata_ex": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _I32, _P, _SZ, _P, _SZ,
-                                     ctypes.POINTER(PkvPlan), _P],
+        "build_extend_metadata_ex": [_I32, _P, _P, ctypes.POINTER(PkvShape), _I32, _I32, _I32, _I32, _P, _SZ, _P,
+                                     _SZ, ctypes.POINTER(PkvPlan), _P],
         "pkv_append": [_P, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P],
         "pkv_rope_append": [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PkvPlan),
                             ctypes.POINTER(PkvShape), _P],

@@ -32,6 +32,47 @@ int device_supported(int dev) {
   return g_dev_ok[dev];
 }
 
+// Per-device compute-unit count, read once per device and cached (the
+// planner sizes its KV splits from it). 0 when it cannot be read.
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+int query_cus(int dev) {
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();   // leave no error behind for the next launch check
+    return 0;
+  }
+  return n > 0 ? n : 0;
+}
+
+// Compute units of the current HIP device, or kNominalCUs (an MI355X) when no
+// device is current or its count cannot be read.
+int current_device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return kNominalCUs;
+  }
+  int n;
+  if (dev < 0 || dev >= kMaxDevices) {
+    n = query_cus(dev);
+  } else {
+    std::call_once(g_cu_once[dev], [dev] { g_cu_count[dev] = query_cus(dev); });
+    n = g_cu_count[dev];
+  }
+  return n > 0 ? n : kNominalCUs;
+}
+
+constexpr int32_t kMaxPlanCUs = 65536;
+
+int resolve_cus(int32_t num_cus, int32_t* out) {
+  if (num_cus < 0 || num_cus > kMaxPlanCUs)
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "num_cus must be in 0..%d (got %d)", kMaxPlanCUs, num_cus);
+  *out = num_cus > 0 ? num_cus : current_device_cus();
+  return PKV_OK;
+}
+
 int check_current_device() {
   int dev = -1;
   const hipError_t e = hipGetDevice(&dev);
@@ -91,13 +132,16 @@ int pkv_device_supported(int device) {
 
 int pkv_extend_metadata_size_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                                 const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
-                                size_t* meta_bytes, size_t* workspace_bytes_out) {
+                                int32_t num_cus, size_t* meta_bytes, size_t* workspace_bytes_out) {
   g_error[0] = 0;
   if (!meta_bytes || !workspace_bytes_out)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_extend_metadata_size: output pointers must not be NULL");
+  int32_t cus = 0;
+  int st = resolve_cus(num_cus, &cus);
+  if (st) return st;
   pkv_plan plan;
-  const int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, flags, decode_splits, 0, nullptr,
-                             0, &plan, meta_bytes);
+  st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, flags, decode_splits, cus, nullptr, 0, &plan,
+                   meta_bytes);
   if (st) return st;
   *workspace_bytes_out = plan.workspace_bytes;
   return PKV_OK;
@@ -106,7 +150,7 @@ int pkv_extend_metadata_size_ex(int32_t batch, const int32_t* prefix_lens_h, con
 int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                              const pkv_shape* shape, int32_t window, int32_t decode_splits, size_t* meta_bytes,
                              size_t* workspace_bytes_out) {
-  return pkv_extend_metadata_size_ex(batch, prefix_lens_h, chunk_lens_h, shape, window, 0, decode_splits,
+  return pkv_extend_metadata_size_ex(batch, prefix_lens_h, chunk_lens_h, shape, window, 0, decode_splits, 0,
                                      meta_bytes, workspace_bytes_out);
 }
 
@@ -114,21 +158,24 @@ int build_extend_metadata(int32_t batch, const int32_t* prefix_lens_h, const int
                           const pkv_shape* shape, int32_t window, int32_t decode_splits, void* meta_host,
                           size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes, pkv_plan* plan_out,
                           pkv_stream_t stream) {
-  return build_extend_metadata_ex(batch, prefix_lens_h, chunk_lens_h, shape, window, 0, decode_splits, meta_host,
-                                  meta_host_bytes, meta_dev, meta_dev_bytes, plan_out, stream);
+  return build_extend_metadata_ex(batch, prefix_lens_h, chunk_lens_h, shape, window, 0, decode_splits, 0,
+                                  meta_host, meta_host_bytes, meta_dev, meta_dev_bytes, plan_out, stream);
 }
 
 int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const int32_t* chunk_lens_h,
                              const pkv_shape* shape, int32_t window, int32_t flags, int32_t decode_splits,
-                             void* meta_host, size_t meta_host_bytes, void* meta_dev, size_t meta_dev_bytes,
-                             pkv_plan* plan_out, pkv_stream_t stream) {
+                             int32_t num_cus, void* meta_host, size_t meta_host_bytes, void* meta_dev,
+                             size_t meta_dev_bytes, pkv_plan* plan_out, pkv_stream_t stream) {
   g_error[0] = 0;
   if (!meta_host || !plan_out)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "build_extend_metadata: meta_host and plan_out must not be NULL");
+  int32_t cus = 0;
+  int st = resolve_cus(num_cus, &cus);
+  if (st) return st;
   size_t total = 0;
   pkv_plan plan;
-  int st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, flags, decode_splits, 0, meta_host,
-                       meta_host_bytes, &plan, &total);
+  st = plan_extend(batch, prefix_lens_h, chunk_lens_h, shape, window, flags, decode_splits, cus, meta_host,
+                   meta_host_bytes, &plan, &total);
   if (st) return st;
   if (meta_dev) {
     if (meta_dev_bytes < total)
@@ -233,6 +280,15 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
     return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: q, pools and out must not be NULL", name);
   if (!(std::isfinite(sm_scale)))
     return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: sm_scale is not finite", name);
+  // the batch arrays: NULL or the plan's own device copies (the kernels take
+  // every offset from the plan; caller device arrays cannot be compared with
+  // it without a host synchronisation)
+  auto planned = [](const void* given, const void* own) { return given == nullptr || given == own; };
+  if (!planned(qo_indptr, plan->qo_indptr) || !planned(kv_indptr, plan->kv_indptr) ||
+      !planned(prefix_lens, plan->prefix_lens))
+    return set_error(PKV_ERR_INVALID_ARGUMENT,
+                     "%s: qo_indptr, kv_indptr and prefix_lens must each be NULL or the plan's own device array",
+                     name);
   if (mask && plan->total_q > 0) {
     if (mask_heads != 1 && mask_heads != shape->num_q_heads)
       return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: mask_heads must be 1 or %d (got %d)", name,
@@ -266,9 +322,8 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
   a.page_table = page_table;
   a.page_table_stride = page_table_stride;
   a.req_pool_indices = req_pool_indices;
-  a.qo_indptr = qo_indptr ? qo_indptr : plan->qo_indptr;
-  a.kv_indptr = kv_indptr ? kv_indptr : plan->kv_indptr;
-  a.prefix_lens = prefix_lens ? prefix_lens : plan->prefix_lens;
+  a.qo_indptr = plan->qo_indptr;
+  a.prefix_lens = plan->prefix_lens;
   a.items = static_cast<const WorkItem*>(plan->items);
   a.split_rows = plan->split_rows;
   a.status = plan->status;

@@ -34,7 +34,7 @@ constexpr int kSplitGranule = 64;
 constexpr int kFuseMaxSlotBlocks = 128;
 // Cap on the KV splits of one prefill tile.
 constexpr int kMaxPrefillSplits = 16;
-// Compute units of an MI355X; the planner sizes splits for this machine.
+// Compute units of an MI355X: the planner's count when no device can be queried.
 constexpr int kNominalCUs = 256;
 // XCDs (each with its own L2); workgroups are dispatched to them round-robin.
 constexpr int kXcds = 8;
@@ -55,11 +55,15 @@ struct alignas(16) WorkItem {
   int32_t part_row;    // -1: write `out`; else partial slot of the tile's first token
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
-constexpr int kSplitBits = 8;   // width of the split index and of the split count in head_split
+// Widths of head_split's split index and split count fields; the KV head takes
+// the bits above them, 15 of them below the sign bit (validate_shape bounds
+// num_kv_heads by kMaxKvHeads accordingly).
+constexpr int kSplitBits = 8;
+static_assert(PKV_MAX_SPLITS < (1 << kSplitBits), "split index and count fit their fields");
+constexpr int kMaxKvHeads = 1 << (31 - 2 * kSplitBits);
 // Non-causal plans put an item's pos0 (the position its causal bound is taken
 // from) past every key, so the kernels' causal test passes for all of them.
-constexpr int32_t kNonCausalPos = 1 << 30;  // split index field of head_split (splits <= PKV_MAX_SPLITS < 256)
-static_assert(PKV_MAX_SPLITS < (1 << kSplitBits), "split index fits its field");
+constexpr int32_t kNonCausalPos = 1 << 30;
 
 // Byte offsets of the sections of the metadata buffer (host staging and its
 // device copy share the layout). Each section starts on a 256-byte boundary.
@@ -118,7 +122,6 @@ struct AttnArgs {
   int32_t page_table_stride;
   const int32_t* req_pool_indices;
   const int32_t* qo_indptr;
-  const int32_t* kv_indptr;
   const int32_t* prefix_lens;
   const WorkItem* items;
   const int32_t* split_rows;

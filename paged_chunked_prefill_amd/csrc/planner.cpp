@@ -25,6 +25,9 @@ int validate_shape(const pkv_shape* s) {
   if (s->num_q_heads < 1 || s->num_kv_heads < 1)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hkv=%d)", s->num_q_heads,
                      s->num_kv_heads);
+  if (s->num_kv_heads >= kMaxKvHeads)
+    return set_error(PKV_ERR_UNSUPPORTED, "num_kv_heads %d is not supported (at most %d)", s->num_kv_heads,
+                     kMaxKvHeads - 1);
   if (s->num_q_heads % s->num_kv_heads)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                      s->num_q_heads, s->num_kv_heads);
@@ -324,6 +327,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     plan->window = window;
     plan->flags = flags;
     plan->slot_blocks = int32_t(std::min<int64_t>(slot_blocks, INT32_MAX));
+    plan->num_cus = num_cus;
     plan->shape = *shape;
     plan->workspace_bytes = workspace_bytes(n_split_rows, hq, max_splits, shape->head_dim, shape->dtype);
   }

@@ -51,10 +51,10 @@ class DeviceCache:
         pt = w.page_table if page_table is None else page_table
         self.page_table = torch.from_numpy(np.ascontiguousarray(pt, dtype=np.int32)).to(device)
 
-    def append_step(self, step: wl.Workload, kv_storage=None, decode_splits: int = 0):
+    def append_step(self, step: wl.Workload, kv_storage=None, decode_splits: int = 0, num_cus: int = 0):
         """Append the step's chunk K/V (generated, or given in storage format)."""
         plan = pkv.build_extend_metadata(step.prefix_lens, step.chunk_lens, shape_of(step), step.window,
-                                         decode_splits, device=self.device)
+                                         decode_splits, device=self.device, num_cus=num_cus)
         if plan.plan.total_q == 0:
             return plan
         if kv_storage is None:
@@ -86,11 +86,12 @@ class DeviceCache:
 
 
 def run_attention(cache: DeviceCache, w: wl.Workload, decode_splits: Optional[int] = None, q: Optional[torch.Tensor] = None,
-                  sm_scale: float = 0.0, plan=None):
-    """Append the chunk (unless a plan is given) and run the attention; returns (out, plan)."""
+                  sm_scale: float = 0.0, plan=None, num_cus: int = 0):
+    """Append the chunk (unless a plan is given) and run the attention; returns (out, plan).
+    ``num_cus`` sizes the plan for that many compute units (0: the device's)."""
     splits = w.decode_splits if decode_splits is None else decode_splits
     if plan is None:
-        plan = cache.append_step(w, decode_splits=splits)
+        plan = cache.append_step(w, decode_splits=splits, num_cus=num_cus)
     if q is None:
         q = upload_q(w, cache.device)
     out = pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, sm_scale=sm_scale)
@@ -117,12 +118,32 @@ def prefill_and_attend(w: wl.Workload, decode_splits: Optional[int] = None, devi
     return out, cache, plan
 
 
-def chunked_prefill(w_full: wl.Workload, chunks, device="cuda", decode_splits: int = 0):
-    """Prefill one request chunk by chunk; returns the concatenated outputs (values) and the cache."""
+def chunked_prefill(w_full: wl.Workload, chunks, device="cuda", decode_splits: int = 0, num_cus: int = 0,
+                    q_full: Optional[torch.Tensor] = None):
+    """Prefill one request chunk by chunk; returns the concatenated outputs and the cache.
+    ``q_full`` ([prompt, Hq, D] on the device) replaces the workload's queries."""
     cache = DeviceCache(w_full, device)
     outs = []
+    pos = 0
     for step in wl.chunked_steps(w_full, chunks):
-        out, _ = run_attention(cache, step, decode_splits)
+        L = int(step.chunk_lens[0])
+        q = None if q_full is None else q_full[pos:pos + L].contiguous()
+        out, _ = run_attention(cache, step, decode_splits, q=q, num_cus=num_cus)
         outs.append(out)
+        pos += L
     torch.cuda.synchronize()
     return torch.cat(outs, 0), cache
+
+
+def spare_page_pools(cache, spare: int = 16, k_fill: float = 1.0, v_fill: float = 16384.0):
+    """Pools of the cache's declared page count followed by `spare` more pages of
+    finite sentinels, returned as views of the declared size: a page id just
+    past the declared pool stays inside the allocation, so a guard that failed
+    to stop it would read (or write) the sentinels, never unmapped memory."""
+    views = []
+    for pool, fill in ((cache.k_pool, k_fill), (cache.v_pool, v_fill)):
+        n = pool.shape[0]
+        big = torch.full((n + spare,) + tuple(pool.shape[1:]), fill, dtype=pool.dtype, device=pool.device)
+        big[:n].copy_(pool)
+        views.append((big, big[:n]))
+    return views

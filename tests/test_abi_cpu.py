@@ -235,6 +235,7 @@ def status_of(fn):
     (dict(s=dict(d=256)), pkv.PKV_ERR_UNSUPPORTED),
     (dict(s=dict(dtype=7)), pkv.PKV_ERR_UNSUPPORTED),
     (dict(s=dict(hq=256, hkv=1)), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(s=dict(hq=32768, hkv=32768, d=64, dtype="fp32")), pkv.PKV_ERR_UNSUPPORTED),   # KV head field of an item
     (dict(splits=33), pkv.PKV_ERR_INVALID_ARGUMENT),
     (dict(splits=-1), pkv.PKV_ERR_INVALID_ARGUMENT),
 ])
@@ -351,11 +352,114 @@ def test_non_causal_flag_errors():
     P, L = np.array([3], np.int32), np.array([2], np.int32)
     mb, wb = ctypes.c_size_t(), ctypes.c_size_t()
     vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
-    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 0, 2, 0, ctypes.byref(mb),
+    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 0, 2, 0, 0, ctypes.byref(mb),
                                            ctypes.byref(wb)) == pkv.PKV_ERR_INVALID_ARGUMENT
     assert "flags" in lib.pkv_last_error().decode()
-    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 5, pkv.PKV_FLAG_NON_CAUSAL, 0,
+    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 5, pkv.PKV_FLAG_NON_CAUSAL, 0, 0,
                                            ctypes.byref(mb), ctypes.byref(wb)) == pkv.PKV_ERR_INVALID_ARGUMENT
     assert "window" in lib.pkv_last_error().decode()
-    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 0, pkv.PKV_FLAG_NON_CAUSAL, 0,
+    assert lib.pkv_extend_metadata_size_ex(1, vp(P), vp(L), ctypes.byref(s), 0, pkv.PKV_FLAG_NON_CAUSAL, 0, 0,
                                            ctypes.byref(mb), ctypes.byref(wb)) == pkv.PKV_OK
+
+
+def test_kv_head_limit_is_the_item_field():
+    """The largest KV head count the work items encode is accepted and decodes
+    back; one more is refused (the field would reach the sign bit)."""
+    ok = pkv.make_shape(32767, 32767, 64, 1, 64, "fp32")
+    p = pkv.build_extend_metadata([0], [1], ok)
+    it = p.host_sections()["items"]
+    assert sorted(it["kv_head"].tolist()) == list(range(32767)) and (it["head_split"] > 0).all()
+    bad = pkv.make_shape(32768, 32768, 64, 1, 64, "fp32")
+    assert status_of(lambda: pkv.build_extend_metadata([0], [1], bad)) == pkv.PKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("P,L,splits,any_split", [([3584], [512], 0, True), ([100, 0, 7, 5000], [1, 300, 65, 1], 0, True),
+                                                  ([20000] * 3, [1] * 3, 8, True), ([6000] * 8, [1000] * 8, 0, False)])
+def test_split_count_field_matches_item_count(P, L, splits, any_split):
+    """Each item's split count field S equals the number of items of its tile
+    (request, KV head, first token), and its split index runs over 0..S-1."""
+    p = pkv.build_extend_metadata(P, L, shape(32, 8, 128, 16, 8000), 4096 if P[0] == 6000 else 0, splits)
+    it = p.host_sections()["items"]
+    S = (it["head_split"] >> pkv.SPLIT_BITS) & ((1 << pkv.SPLIT_BITS) - 1)
+    tiles = {}
+    for x, s_ in zip(it, S):
+        tiles.setdefault((int(x["req"]), int(x["kv_head"]), int(x["q_begin"])), []).append((int(x["split"]), int(s_)))
+    assert any(len(v) > 1 for v in tiles.values()) == any_split
+    for v in tiles.values():
+        assert all(s_ == len(v) for _, s_ in v)
+        assert sorted(k for k, _ in v) == list(range(len(v)))
+
+
+def test_plan_sized_for_the_given_compute_units():
+    """The work list follows the compute-unit count: a 32-unit device gets the
+    headline chunk's 32 tiles unsplit (one item per unit), 256 units split them;
+    one-token rows get ceil(2 * CUs / base items) splits."""
+    s16 = shape(16, 4, 128, 64, 1000)
+    small = pkv.build_extend_metadata([3584], [512], s16, num_cus=32)
+    assert small.plan.num_cus == 32
+    assert small.plan.n_items == 32 and small.plan.n_split_rows == 0 and small.plan.workspace_bytes == 0
+    big = pkv.build_extend_metadata([3584], [512], s16, num_cus=256)
+    assert big.plan.num_cus == 256 and 32 < big.plan.n_items <= 256 and big.plan.n_split_rows == 512
+    mid = pkv.build_extend_metadata([3584], [512], s16, num_cus=80)
+    assert 32 < mid.plan.n_items <= 80
+    P, L = np.full(4, 20000, np.int32), np.ones(4, np.int32)
+    for cus, want in ((32, 2), (64, 4), (256, 16), (1024, 32)):
+        p = pkv.build_extend_metadata(P, L, shape(32, 8, 128, 16, 8000), num_cus=cus)
+        assert p.plan.max_splits == want, (cus, p.plan.max_splits)
+    # the size query plans the same list
+    for cus in (32, 256):
+        mb, wb = pkv.extend_metadata_size([3584], [512], s16, num_cus=cus)
+        p = pkv.build_extend_metadata([3584], [512], s16, num_cus=cus)
+        assert mb == p.meta_host.size and wb == p.plan.workspace_bytes
+
+
+def test_plan_without_device_uses_nominal_cus():
+    """With no HIP device to query (this host), num_cus = 0 sizes the list for
+    an MI355X's 256 compute units."""
+    p = pkv.build_extend_metadata([3584], [512], shape(16, 4, 128, 64, 1000))
+    assert p.plan.num_cus == 256
+
+
+@pytest.mark.parametrize("cus", [-1, 65537])
+def test_num_cus_out_of_range_rejected(cus):
+    assert status_of(lambda: pkv.build_extend_metadata([3], [2], shape(), num_cus=cus)) == \
+        pkv.PKV_ERR_INVALID_ARGUMENT
+    assert status_of(lambda: pkv.extend_metadata_size([3], [2], shape(), num_cus=cus)) == \
+        pkv.PKV_ERR_INVALID_ARGUMENT
+
+
+def test_batch_arrays_must_be_the_plans_own():
+    """paged_extend_attn(_masked) takes qo_indptr / kv_indptr / prefix_lens only
+    as NULL or the plan's own device arrays; any other pointer is refused before
+    any HIP call. (The plan's device pointers are stand-ins here: nothing runs.)"""
+    lib = pkv.lib()
+    s = shape()
+    p = pkv.build_extend_metadata([3], [2], s)
+    assert p.plan.workspace_bytes == 0
+    fake = p.plan
+    fake.qo_indptr, fake.kv_indptr, fake.prefix_lens = 0x10000, 0x20000, 0x30000
+    fake.items, fake.status = 0x40000, 0x50000
+    d = ctypes.c_void_p(0x1000)
+    other = ctypes.c_void_p(0x60000)
+
+    def attn(qo, kv, pre):
+        return lib.paged_extend_attn(d, d, d, d, 4, None, qo, kv, pre, 0, 0.0, ctypes.byref(fake), ctypes.byref(s), d,
+                                     None, 0, None)
+
+    def masked(qo, kv, pre):
+        return lib.paged_extend_attn_masked(d, d, d, d, 4, None, qo, kv, pre, 0, 0.0, d, 1, 1, 8,
+                                            ctypes.byref(fake), ctypes.byref(s), d, None, 0, None)
+
+    own = [ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)]
+    for fn in (attn, masked):
+        for i in range(3):
+            args = [None, None, None]
+            args[i] = other
+            assert fn(*args) == pkv.PKV_ERR_INVALID_ARGUMENT
+            assert "plan's own device array" in lib.pkv_last_error().decode()
+        # swapped arrays are refused too
+        assert fn(own[1], own[0], None) == pkv.PKV_ERR_INVALID_ARGUMENT
+        # NULL or the plan's own pass this check; the call then stops at the device check (no GPU here)
+        for args in ([None, None, None], own):
+            assert fn(*args) == pkv.PKV_ERR_HIP, lib.pkv_last_error().decode()
+            assert "device" in lib.pkv_last_error().decode()

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import paged_chunked_prefill_amd as pkv
-    from gpu_harness import DeviceCache, from_dev, shape_of, upload_q, values_of
+    from gpu_harness import DeviceCache, from_dev, shape_of, spare_page_pools, upload_q, values_of
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -155,19 +155,23 @@ def test_long_launch_takes_the_append_kernel():
 
 
 def test_fused_bad_page_is_flagged_and_not_written():
-    """A new position whose page id lies outside the pool: the status word says
-    so and no pool byte is written for it (the two-call path skips it too)."""
+    """A new position whose page id lies just past the pool (inside a spare,
+    sentinel-filled allocation): the status word says so and no pool byte is
+    written for it (the two-call path skips it too); the spare pages keep their
+    sentinels, so a failed guard would show as changed bytes, not a fault."""
     P, L = np.array([32], np.int32), np.array([32], np.int32)
     w = wl.Workload("bad", 45, "bf16", 8, 2, 128, 16, 16, 0, P, L, wl.shuffled_page_table(45, 16, P + L, 16))
     bad = w.page_table.copy()
-    bad[0, 3] = 10_000                        # positions 48..63: out of the pool
-    caches = []
+    bad[0, 3] = 20                            # positions 48..63: past the declared 16 pages
+    pools = []
     for _ in range(2):
         c = DeviceCache(w)
         c.fill_prefix(w)
         c.page_table = torch.from_numpy(np.ascontiguousarray(bad, np.int32)).cuda()
-        caches.append(c)
-    two, fused = caches
+        (kbig, kp), (vbig, vp) = spare_page_pools(c)
+        c.k_pool, c.v_pool = kp, vp
+        pools.append((c, kbig, vbig))
+    (two, two_kbig, two_vbig), (fused, fused_kbig, fused_vbig) = pools
     plan = pkv.build_extend_metadata(P, L, shape_of(w), 0, 0, device="cuda")
     q = upload_q(w)
     kn, vn = two._gather_new_kv(w)
@@ -179,8 +183,10 @@ def test_fused_bad_page_is_flagged_and_not_written():
     torch.cuda.synchronize()
     assert pkv.read_status(plan2) == pkv.PKV_STATUS_BAD_PAGE
     assert not torch.isnan(out.float()).any()
-    for a, b in ((fused.k_pool, two.k_pool), (fused.v_pool, two.v_pool)):
+    for a, b in ((fused_kbig, two_kbig), (fused_vbig, two_vbig)):
         assert np.array_equal(_bits(a), _bits(b))
+    for kbig, vbig in ((two_kbig, two_vbig), (fused_kbig, fused_vbig)):
+        assert bool((kbig[16:] == 1.0).all()) and bool((vbig[16:] == 16384.0).all()), "a spare page was written"
 
 
 def test_fused_rejects_overlap_and_null():

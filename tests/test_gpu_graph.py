@@ -35,15 +35,29 @@ def _workload(name):
     return wl.config4(mid_page=True)   # window, no splits
 
 
+def _pool_rows(cache, w, dev):
+    """The cache's page table as rows of a larger request pool in a shuffled
+    order, with req_pool_indices pointing each request at its row."""
+    rows = 3 * w.batch + 5
+    perm = np.random.default_rng(17).permutation(rows)[:w.batch].astype(np.int32)
+    big = np.full((rows, w.page_table.shape[1]), -1, np.int32)
+    big[perm] = w.page_table
+    pkv.check_req_pool_indices(perm, rows, w.batch)
+    cache.page_table = torch.from_numpy(big).to(dev)
+    return torch.from_numpy(perm).to(dev)
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_append"])
-@pytest.mark.parametrize("name", ["ragged_splits", "decode_splits", "window"])
-def test_graph_replay_matches_eager(name, fused):
+@pytest.mark.parametrize("name,pool_rows", [("ragged_splits", False), ("decode_splits", False), ("window", False),
+                                            ("ragged_splits", True), ("decode_splits", True)])
+def test_graph_replay_matches_eager(name, pool_rows, fused):
     w = _workload(name)
     dev = torch.device("cuda", torch.cuda.current_device())
-    print(f"[graph] {name} fused={fused}: P={list(w.prefix_lens)[:4]} L={list(w.chunk_lens)[:4]} batch={w.batch}",
-          flush=True)
+    print(f"[graph] {name} fused={fused} req_pool_indices={pool_rows}: P={list(w.prefix_lens)[:4]} "
+          f"L={list(w.chunk_lens)[:4]} batch={w.batch}", flush=True)
     cache = DeviceCache(w, dev)
     cache.fill_prefix(w)
+    rpi = _pool_rows(cache, w, dev) if pool_rows else None
     plan = pkv.build_extend_metadata(w.prefix_lens, w.chunk_lens, shape_of(w), w.window, w.decode_splits, device=dev)
     kn, vn = cache._gather_new_kv(w)
     q = upload_q(w, dev)
@@ -53,10 +67,11 @@ def test_graph_replay_matches_eager(name, fused):
     def path():
         if fused:   # paged_extend_attn_append: one launch for these plans where it fuses
             pkv.paged_extend_attn_append(q, kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out,
-                                         workspace=ws)
+                                         workspace=ws, req_pool_indices=rpi)
             return
-        pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan)
-        pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out, workspace=ws)
+        pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan, req_pool_indices=rpi)
+        pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out, workspace=ws,
+                              req_pool_indices=rpi)
 
     path()                  # eager: the reference result (appending again later writes the same bytes)
     torch.cuda.synchronize()
