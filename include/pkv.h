@@ -325,6 +325,28 @@ int paged_extend_attn_append(const void* q, const void* k_new, const void* v_new
                              int32_t window, float sm_scale, const pkv_plan* plan, const pkv_shape* shape,
                              void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
+/*
+ * paged_extend_attn_noalloc -- paged_extend_attn without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). The split
+ * partials go to a static device array of PKV_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device for the life of the process; nothing is
+ * allocated or freed by the call. All calls on one device share that array,
+ * so calls that overlap in time on one device (other streams, other threads)
+ * race and must not be made. The array needs no clearing between calls: every
+ * byte a call reads was written earlier in the same call.
+ * Every argument as paged_extend_attn. Errors as paged_extend_attn, plus
+ * PKV_ERR_WORKSPACE when plan->workspace_bytes exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES (a plan with that many split partials needs
+ * paged_extend_attn and a workspace), PKV_ERR_UNSUPPORTED for a device index
+ * of 64 or more, and PKV_ERR_HIP when the array's address cannot be read.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_extend_attn_noalloc(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                              const pkv_plan* plan, const pkv_shape* shape, void* out, pkv_stream_t stream);
+
 /* Copies the plan's device status word to *status_out after synchronising the
  * stream (a diagnostic; not needed on the hot path). */
 int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream);

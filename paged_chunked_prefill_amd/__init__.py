@@ -25,8 +25,8 @@ import numpy as np
 from . import _abi
 from ._abi import (PKV_DTYPE_BF16, PKV_DTYPE_FP32, PKV_ERR_HIP, PKV_ERR_INVALID_ARGUMENT,  # noqa: F401
                    PKV_FLAG_NON_CAUSAL,
-                   PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_MAX_SPLITS, PKV_OK, PKV_STATUS_BAD_PAGE,
-                   PkvPlan, PkvShape)
+                   PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_MAX_SPLITS, PKV_NOALLOC_SCRATCH_BYTES, PKV_OK,
+                   PKV_STATUS_BAD_PAGE, PkvPlan, PkvShape)
 
 _lib = _abi.load()
 
@@ -374,6 +374,29 @@ def paged_extend_attn_masked(q, k_pool, v_pool, page_table, plan: ExtendPlan, ma
                                          mask.shape[3], ctypes.byref(plan.plan), ctypes.byref(s),
                                          ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes,
                                          _stream_handle(stream, q.device)), "paged_extend_attn_masked")
+    return out
+
+
+def paged_extend_attn_noalloc(q, k_pool, v_pool, page_table, plan: ExtendPlan, out, window: Optional[int] = None,
+                              sm_scale: float = 0.0, req_pool_indices=None, stream=None):
+    """paged_extend_attn with the split partials in the library's static
+    per-device scratch (no workspace, nothing allocated; ``out`` must be given).
+    Calls that overlap in time on one device race on that scratch."""
+    s = plan.shape
+    dt = _torch_dtype(s.dtype)
+    tq = plan.plan.total_q
+    _expect(q, (tq, s.num_q_heads, s.head_dim), dt, "q")
+    _expect(k_pool, _pool_shape(s), dt, "k_pool")
+    _expect(v_pool, _pool_shape(s), dt, "v_pool")
+    _check_tables(page_table, plan, req_pool_indices)
+    _expect(out, (tq, s.num_q_heads, s.head_dim), dt, "out")
+    opt = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    _check(_lib.paged_extend_attn_noalloc(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_pool.data_ptr()),
+                                          ctypes.c_void_p(v_pool.data_ptr()), ctypes.c_void_p(page_table.data_ptr()),
+                                          page_table.shape[1], opt(req_pool_indices), None, None, None,
+                                          plan.plan.window if window is None else int(window), float(sm_scale),
+                                          ctypes.byref(plan.plan), ctypes.byref(s), ctypes.c_void_p(out.data_ptr()),
+                                          _stream_handle(stream, q.device)), "paged_extend_attn_noalloc")
     return out
 
 

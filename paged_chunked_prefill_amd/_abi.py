@@ -14,10 +14,12 @@ PKV_DTYPE_FP32 = 1
 PKV_STATUS_BAD_PAGE = 1
 PKV_FLAG_NON_CAUSAL = 1
 PKV_MAX_SPLITS = 32
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("pkv_extend_metadata_size", "build_extend_metadata", "pkv_extend_metadata_size_ex",
            "build_extend_metadata_ex", "pkv_append", "pkv_rope_append",
-           "paged_extend_attn", "paged_extend_attn_masked", "paged_extend_attn_append", "pkv_read_status",
+           "paged_extend_attn", "paged_extend_attn_masked", "paged_extend_attn_append", "paged_extend_attn_noalloc",
+           "pkv_read_status",
            "pkv_last_error",
            "pkv_device_supported")
 
@@ -77,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      _I32, ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P, _SZ, _P],
         "paged_extend_attn_append": [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, ctypes.c_float,
                                      ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P, _SZ, _P],
+        "paged_extend_attn_noalloc": [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, ctypes.c_float,
+                                      ctypes.POINTER(PkvPlan), ctypes.POINTER(PkvShape), _P, _P],
         "pkv_read_status": [ctypes.POINTER(PkvPlan), ctypes.POINTER(_I32), _P],
         "pkv_last_error": [],
         "pkv_device_supported": [ctypes.c_int],

@@ -118,6 +118,40 @@ int set_error(int status, const char* fmt, ...) {
 
 }  // namespace pkv
 
+// Scratch of paged_extend_attn_noalloc: the split partials of one call, in a
+// file-scope device array instead of a caller workspace. Each device holds its
+// own copy for the life of the process; calls on one device share it. In host
+// code the array's name is not a device address: the address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace pkv {
+namespace {
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array.
+int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(PKV_ERR_HIP, "no current HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(PKV_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return set_error(PKV_ERR_HIP, "device %d: cannot get the scratch array's address: %s", dev,
+                     hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+}  // namespace pkv
+
 using namespace pkv;
 
 extern "C" {
@@ -416,6 +450,27 @@ int paged_extend_attn_append(const void* q, const void* k_new, const void* v_new
   return extend_attn_call(name, q, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, nullptr, nullptr,
                           nullptr, window, sm_scale, nullptr, 1, 1, 0, plan, shape, out, workspace, workspace_bytes,
                           stream, plan->total_q > 0 ? k_new : nullptr, v_new);
+}
+
+int paged_extend_attn_noalloc(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* req_pool_indices, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* prefix_lens, int32_t window, float sm_scale,
+                              const pkv_plan* plan, const pkv_shape* shape, void* out, pkv_stream_t stream) {
+  static const char* name = "paged_extend_attn_noalloc";
+  g_error[0] = 0;
+  if (!plan) return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: plan is NULL", name);
+  if (plan->workspace_bytes > size_t(PKV_NOALLOC_SCRATCH_BYTES))
+    return set_error(PKV_ERR_WORKSPACE, "%s: the plan needs %zu workspace bytes, more than the %zu-byte static scratch",
+                     name, plan->workspace_bytes, size_t(PKV_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (plan->workspace_bytes > 0) {
+    int st = check_current_device();
+    if (st) return st;
+    if ((st = static_scratch(&ws))) return st;
+  }
+  return extend_attn_call(name, q, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, qo_indptr,
+                          kv_indptr, prefix_lens, window, sm_scale, nullptr, 1, 1, 0, plan, shape, out, ws,
+                          ws ? size_t(PKV_NOALLOC_SCRATCH_BYTES) : 0, stream);
 }
 
 int pkv_read_status(const pkv_plan* plan, int32_t* status_out, pkv_stream_t stream) {

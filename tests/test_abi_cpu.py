@@ -463,3 +463,22 @@ def test_batch_arrays_must_be_the_plans_own():
         for args in ([None, None, None], own):
             assert fn(*args) == pkv.PKV_ERR_HIP, lib.pkv_last_error().decode()
             assert "device" in lib.pkv_last_error().decode()
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch():
+    """paged_extend_attn_noalloc: a plan whose split partials exceed the static
+    scratch is refused with PKV_ERR_WORKSPACE before any HIP call; a NULL plan
+    with PKV_ERR_INVALID_ARGUMENT. (Stand-in device pointers: nothing runs.)"""
+    lib = pkv.lib()
+    s = shape(64, 8, 128, 16, 1 << 20)
+    P, L = np.full(1000, 20000, np.int32), np.ones(1000, np.int32)
+    p = pkv.build_extend_metadata(P, L, s, 0, 8)
+    assert p.plan.workspace_bytes > pkv.PKV_NOALLOC_SCRATCH_BYTES
+    fake = p.plan
+    fake.qo_indptr, fake.kv_indptr, fake.prefix_lens, fake.items, fake.status = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000
+    d = ctypes.c_void_p(0x1000)
+    st = lib.paged_extend_attn_noalloc(d, d, d, d, 2048, None, None, None, None, 0, 0.0, ctypes.byref(fake),
+                                       ctypes.byref(s), d, None)
+    assert st == pkv.PKV_ERR_WORKSPACE and "static scratch" in lib.pkv_last_error().decode()
+    assert lib.paged_extend_attn_noalloc(d, d, d, d, 2048, None, None, None, None, 0, 0.0, None, ctypes.byref(s), d,
+                                         None) == pkv.PKV_ERR_INVALID_ARGUMENT
