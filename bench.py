@@ -155,6 +155,10 @@ def main():
                          "of pkv_append) before the attention; reports that kernel's HBM rate")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="rocprofv3 --pmc output directory (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "SQ_INSTS_VALU, SQ_INSTS_MFMA, GRBM_GUI_ACTIVE) of --workload: print the attention kernel's "
+                         "executed MFMA work per launch against the algorithmic FLOPs, and its MFMA busy fraction")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE of --workload; the same "
                          "two of copy_calibration): print the attention kernel's HBM traffic per launch as JSON")
@@ -163,6 +167,8 @@ def main():
         return summarize_stats(args)
     if args.summarize_traffic:
         return summarize_traffic(args)
+    if args.summarize_mfma:
+        return summarize_mfma(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -287,6 +293,7 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.warmup, nsteps):
         step(s, False)
+    t_enq = time.perf_counter() - t0      # host time to plan and enqueue the K steps
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
@@ -374,6 +381,7 @@ def main():
                    "batches_per_step": len(B),
                    "query_tokens_per_step": tokens, "flops_per_step": flops},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "host_enqueue_ms_per_step": round(1e3 * t_enq / args.steps, 4),
         "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
         "attn_only": {"ms_per_step": round(attn_total_ms, 4), "tflops": round(attn_tflops, 3),
                       "mfma_peak_frac": round(attn_tflops / MFMA_PEAK_BF16, 4),
@@ -458,14 +466,20 @@ def _counter_means(directory, match):
     import collections
     import csv
     per = collections.defaultdict(float)
+    dur = {}
     with open(os.path.join(directory, "run_counter_collection.csv")) as f:
         for r in csv.DictReader(f):
             if match in r["Kernel_Name"]:
-                per[(r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
+                key, v = (r["Dispatch_Id"], r["Counter_Name"]), float(r["Counter_Value"])
+                # GRBM counters count GPU-wide cycles: the instances are copies, take the largest
+                per[key] = max(per[key], v) if r["Counter_Name"].startswith("GRBM_") else per[key] + v
+                dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     out = collections.defaultdict(list)
     for (_, c), v in per.items():
         out[c].append(v)
-    return {c: sum(v) / len(v) for c, v in out.items()}, len({d for d, _ in per})
+    means = {c: sum(v) / len(v) for c, v in out.items()}
+    means["duration_ns"] = sum(dur.values()) / max(1, len(dur))
+    return means, len({d for d, _ in per})
 
 
 def summarize_traffic(args):
@@ -482,6 +496,38 @@ def summarize_traffic(args):
            "copy_fetch_kib": round(cal_f["FETCH_SIZE"], 1), "copy_write_kib": round(cal_w["WRITE_SIZE"], 1),
            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
            "traffic_bytes_per_launch": round((fetch["FETCH_SIZE"] * fs + write["WRITE_SIZE"] * ws) * 1024)}
+    print(json.dumps(out, indent=1))
+
+
+def summarize_mfma(args):
+    """Executed MFMA work of the attention kernel per launch (rocprofv3 counters,
+    summed over the kernel's instances and averaged over its dispatches)
+    against the workload's algorithmic FLOPs (4 D Hq per visible pair), the
+    MFMA busy fraction (busy cycles per SIMD over one XCD's active cycles) and
+    the clock the kernel ran at (active cycles over the dispatch's duration)."""
+    import numpy as np
+    c, n = _counter_means(args.summarize_mfma, "extend_attn")
+    w, batches, _, desc = workload(args.workload)
+    alg = [4 * w.head_dim * w.num_q_heads * visible_pairs(np.asarray(b.prefix_lens), np.asarray(b.chunk_lens), b.window)
+           for b in batches]
+    alg_per_launch = sum(alg) / len(alg)
+    simds = 256 * 4
+    executed = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    # GRBM_GUI_ACTIVE here sums the busy cycles of the 8 XCDs (a fill kernel of 176 us reads
+    # 3.44e6 = 8 x 2.44 GHz x 176 us), so one XCD's cycles, the clock the kernel ran at, are an eighth
+    xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8
+    out = {"workload": args.workload, "kernel": "extend_attn", "kernel_source_sha256_16": kernel_hash(),
+           "dispatches": n, "launches_per_step": len(alg),
+           "mfma_flops_executed_per_launch": round(executed),
+           "mfma_flops_algorithmic_per_launch": round(alg_per_launch),
+           "executed_over_algorithmic": round(executed / alg_per_launch, 4),
+           "mfma_busy_frac": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * simds), 4),
+           "kernel_us_per_launch": round(c["duration_ns"] / 1e3, 3),
+           "clock_ghz": round(xcd_cycles / c["duration_ns"], 3),
+           "mfma_tflops_executed": round(executed / c["duration_ns"] / 1e3, 1),
+           "gui_active_cycles_per_launch": round(c["GRBM_GUI_ACTIVE"]),
+           "valu_insts_per_launch": round(c.get("SQ_INSTS_VALU", 0)),
+           "mfma_insts_per_launch": round(c.get("SQ_INSTS_MFMA", 0))}
     print(json.dumps(out, indent=1))
 
 

@@ -59,76 +59,87 @@ struct Tile {
 
 int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
 
+// The planner's buffers, kept per thread and reused from call to call: after a
+// thread's first few plans no call allocates.
+struct Scratch {
+  std::vector<Tile> tiles;
+  std::vector<int32_t> qo_start, tile_splits, req_splits, group_base, gid, split_rows, xcd_count, xcd_start;
+  std::vector<WorkItem> items, ordered;
+  std::vector<int64_t> cost, group_cost;
+  std::vector<uint64_t> packed, gpacked;
+  std::vector<uint8_t> xcd_of;
+  std::vector<uint32_t> by_xcd;
+};
+
+Scratch& scratch() {
+  static thread_local Scratch s;
+  return s;
+}
+
 // Reorder items so that position i (dispatched to XCD i % kXcds) holds work of
 // the locality group assigned to that XCD; see the dispatch-order comment in
-// plan_extend. Falls back to plain longest-first when there are fewer items
-// than XCDs.
-template <class Cost>
-std::vector<WorkItem> xcd_order(const std::vector<WorkItem>& in, Cost cost) {
+// plan_extend. gid[i] is item i's group, numbered 0..ng-1 in (request, KV head,
+// split) order. Falls back to plain longest-first when there are fewer items
+// than twice the XCDs.
+void xcd_order(Scratch& sc, int32_t ng) {
+  const std::vector<WorkItem>& in = sc.items;
+  const std::vector<int64_t>& c = sc.cost;
+  std::vector<WorkItem>& out = sc.ordered;
   const size_t n = in.size();
-  std::vector<int64_t> c(n);
-  for (size_t i = 0; i < n; ++i) c[i] = cost(in[i]);
+  out.clear();
   // Longest first, ties in the planner's order: one integer sort of
   // (max cost - cost, index) packed into 64 bits (costs < 2^31 per item).
   const int64_t cmax = n ? *std::max_element(c.begin(), c.end()) : 0;
-  std::vector<uint64_t> packed(n);
-  for (size_t i = 0; i < n; ++i) packed[i] = (uint64_t(cmax - c[i]) << 32) | uint64_t(i);
-  std::sort(packed.begin(), packed.end());
-  std::vector<uint32_t> ord(n);
-  for (size_t i = 0; i < n; ++i) ord[i] = uint32_t(packed[i] & 0xffffffffu);
-  std::vector<WorkItem> out;
-  out.reserve(n);
+  sc.packed.resize(n);
+  for (size_t i = 0; i < n; ++i) sc.packed[i] = (uint64_t(cmax - c[i]) << 32) | uint64_t(i);
+  std::sort(sc.packed.begin(), sc.packed.end());
   if (n < size_t(kXcds) * 2) {
-    for (uint32_t i : ord) out.push_back(in[i]);
-    return out;
+    for (uint64_t pk : sc.packed) out.push_back(in[pk & 0xffffffffu]);
+    return;
   }
-  // locality groups: items with equal (request, KV head, split)
-  std::vector<std::pair<uint64_t, uint32_t>> keyed(n);
-  for (size_t i = 0; i < n; ++i) {
-    // (the split count bits stay out of the key: the groups are as before)
-    const uint32_t hk = uint32_t(in[i].head_split) >> (2 * kSplitBits), k = uint32_t(in[i].head_split) & 0xffu;
-    keyed[i] = {(uint64_t(uint32_t(in[i].req)) << 32) | (uint64_t(hk) << kSplitBits) | k, uint32_t(i)};
-  }
-  std::sort(keyed.begin(), keyed.end());
-  std::vector<uint32_t> group_of(n);
-  std::vector<int64_t> group_cost;
-  for (size_t k = 0; k < n; ++k) {
-    if (k == 0 || keyed[k].first != keyed[k - 1].first) group_cost.push_back(0);
-    group_of[keyed[k].second] = uint32_t(group_cost.size() - 1);
-    group_cost.back() += c[keyed[k].second];
-  }
-  // groups to XCDs: largest first, each to the least-loaded XCD
-  const size_t ng = group_cost.size();
-  const int64_t gmax = *std::max_element(group_cost.begin(), group_cost.end());
-  std::vector<uint64_t> gpacked(ng);
-  for (size_t g = 0; g < ng; ++g) gpacked[g] = (uint64_t(gmax - group_cost[g]) << 32) | uint64_t(g);
-  std::sort(gpacked.begin(), gpacked.end());
+  // groups to XCDs: largest first (ties in group order), each to the least-loaded XCD
+  sc.group_cost.assign(size_t(ng), 0);
+  for (size_t i = 0; i < n; ++i) sc.group_cost[size_t(sc.gid[i])] += c[i];
+  const int64_t gmax = *std::max_element(sc.group_cost.begin(), sc.group_cost.end());
+  sc.gpacked.resize(size_t(ng));
+  for (int32_t g = 0; g < ng; ++g) sc.gpacked[size_t(g)] = (uint64_t(gmax - sc.group_cost[size_t(g)]) << 32) | uint64_t(g);
+  std::sort(sc.gpacked.begin(), sc.gpacked.end());
   int64_t load[kXcds] = {};
-  std::vector<uint8_t> xcd_of(group_cost.size());
-  for (uint64_t gp : gpacked) {
+  sc.xcd_of.resize(size_t(ng));
+  for (uint64_t gp : sc.gpacked) {
     const uint32_t g = uint32_t(gp & 0xffffffffu);
     int best = 0;
     for (int x = 1; x < kXcds; ++x)
       if (load[x] < load[best]) best = x;
-    load[best] += group_cost[g];
-    xcd_of[g] = uint8_t(best);
+    load[best] += sc.group_cost[g];
+    sc.xcd_of[g] = uint8_t(best);
   }
-  // per-XCD lists in longest-first order, then dealt out round-robin
-  std::vector<uint32_t> per[kXcds];
-  for (uint32_t i : ord) per[xcd_of[group_of[i]]].push_back(i);
-  size_t next[kXcds] = {};
+  // per-XCD lists in longest-first order (one flat array, counted first), then
+  // dealt out round-robin
+  int32_t cnt[kXcds] = {}, at[kXcds];
+  for (size_t i = 0; i < n; ++i) ++cnt[sc.xcd_of[size_t(sc.gid[i])]];
+  at[0] = 0;
+  for (int x = 1; x < kXcds; ++x) at[x] = at[x - 1] + cnt[x - 1];
+  int32_t start[kXcds];
+  std::copy(at, at + kXcds, start);
+  sc.by_xcd.resize(n);
+  for (uint64_t pk : sc.packed) {
+    const uint32_t i = uint32_t(pk & 0xffffffffu);
+    sc.by_xcd[size_t(at[sc.xcd_of[size_t(sc.gid[i])]]++)] = i;
+  }
+  int32_t next[kXcds] = {};
+  out.reserve(n);
   for (size_t i = 0; out.size() < n; ++i) {
     int x = int(i % kXcds);
-    if (next[x] >= per[x].size()) {
+    if (next[x] >= cnt[x]) {
       // this XCD's list is used up: hand its slot the next item of the fullest list
       int best = -1;
       for (int y = 0; y < kXcds; ++y)
-        if (next[y] < per[y].size() && (best < 0 || per[y].size() - next[y] > per[best].size() - next[best])) best = y;
+        if (next[y] < cnt[y] && (best < 0 || cnt[y] - next[y] > cnt[best] - next[best])) best = y;
       x = best;
     }
-    out.push_back(in[per[x][next[x]++]]);
+    out.push_back(in[sc.by_xcd[size_t(start[x] + next[x]++)]]);
   }
-  return out;
 }
 
 }  // namespace
@@ -171,11 +182,14 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     max_kv = std::max<int32_t>(max_kv, int32_t(N));
   }
 
-  std::vector<int32_t> qo_start(batch, 0);
+  Scratch& sc = scratch();
+  std::vector<int32_t>& qo_start = sc.qo_start;
+  qo_start.assign(size_t(batch), 0);
   for (int32_t b = 1; b < batch; ++b) qo_start[b] = qo_start[b - 1] + chunk_lens[b - 1];
 
   // ---- tiles of GQA-packed query rows and their visible key ranges
-  std::vector<Tile> tiles;
+  std::vector<Tile>& tiles = sc.tiles;
+  tiles.clear();
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t P = prefix_lens[b], L = chunk_lens[b];
     for (int32_t q0 = 0; q0 < L; q0 += tile_tokens) {
@@ -241,26 +255,55 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     unit = lo;
   }
 
-  std::vector<WorkItem> items;
-  items.reserve(size_t(base_items) * 2);
-  std::vector<int32_t> split_rows;  // pairs (token, splits)
-  int32_t n_split_rows = 0, max_splits = 1;
-  for (const Tile& t : tiles) {
-    const int32_t g0 = t.kv_lo / kSplitGranule;
-    const int32_t granules = granules_of(t);
+  // splits of every tile; a request's locality groups are (KV head, split) pairs
+  // up to its largest split count, numbered in (request, KV head, split) order
+  std::vector<int32_t>& tile_splits = sc.tile_splits;
+  tile_splits.resize(tiles.size());
+  std::vector<int32_t>& req_splits = sc.req_splits;
+  req_splits.assign(size_t(batch), 0);
+  int64_t n_alloc = 0;
+  for (size_t ti = 0; ti < tiles.size(); ++ti) {
+    const Tile& t = tiles[ti];
     int32_t splits = 1;
     if (t.one_token) {
       splits = one_token_splits(t);
     } else if (unit > 0) {
-      const int64_t want = (int64_t(granules) * waves_of(t) + unit - 1) / unit;
+      const int64_t want = (int64_t(granules_of(t)) * waves_of(t) + unit - 1) / unit;
       splits = int32_t(std::max<int64_t>(1, std::min(want, prefill_cap(t))));
     }
+    tile_splits[ti] = splits;
+    req_splits[size_t(t.req)] = std::max(req_splits[size_t(t.req)], splits);
+    n_alloc += int64_t(hkv) * splits;
+  }
+  std::vector<int32_t>& group_base = sc.group_base;
+  group_base.resize(size_t(batch));
+  int32_t n_groups = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    group_base[size_t(b)] = n_groups;
+    n_groups += hkv * req_splits[size_t(b)];
+  }
+
+  std::vector<WorkItem>& items = sc.items;
+  items.clear();
+  items.reserve(size_t(n_alloc));
+  std::vector<int32_t>& gid = sc.gid;
+  gid.clear();
+  gid.reserve(size_t(n_alloc));
+  std::vector<int32_t>& split_rows = sc.split_rows;  // pairs (token, splits)
+  split_rows.clear();
+  int32_t n_split_rows = 0, max_splits = 1;
+  for (size_t ti = 0; ti < tiles.size(); ++ti) {
+    const Tile& t = tiles[ti];
+    const int32_t g0 = t.kv_lo / kSplitGranule;
+    const int32_t granules = granules_of(t);
+    const int32_t splits = tile_splits[ti];
     int32_t part_row = -1;
     if (splits > 1) {
       part_row = n_split_rows;
       n_split_rows += t.q_count;
       max_splits = std::max(max_splits, splits);
     }
+    const int32_t rs = req_splits[size_t(t.req)], gb = group_base[size_t(t.req)];
     for (int32_t h = 0; h < hkv; ++h) {
       for (int32_t k = 0; k < splits; ++k) {
         WorkItem it;
@@ -274,12 +317,13 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
           it.kv_end = t.kv_hi;
         } else {
           const int32_t ga = g0 + int32_t(int64_t(k) * granules / splits);
-          const int32_t gb = g0 + int32_t(int64_t(k + 1) * granules / splits);
+          const int32_t gbk = g0 + int32_t(int64_t(k + 1) * granules / splits);
           it.kv_begin = std::max(t.kv_lo, ga * kSplitGranule);
-          it.kv_end = std::min(t.kv_hi, gb * kSplitGranule);
+          it.kv_end = std::min(t.kv_hi, gbk * kSplitGranule);
         }
         it.part_row = part_row;
         items.push_back(it);
+        gid.push_back(gb + h * rs + k);
       }
     }
     if (splits > 1) {
@@ -297,18 +341,22 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   // one XCD (groups assigned greedily to the least-loaded XCD, largest first),
   // so the tiles that stream one KV head stay together in one L2. Within an XCD
   // the longest items go first; an item's time grows with its key range times
-  // its live 32-row waves.
-  auto cost = [group](const WorkItem& a) {
-    return int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
-  };
-  items = xcd_order(items, cost);
-  const int32_t n_items = int32_t(items.size());
+  // its live 32-row waves. A size query (no meta_host) needs no order.
+  std::vector<int64_t>& cost = sc.cost;
+  cost.resize(items.size());
+  for (size_t i = 0; i < items.size(); ++i) {
+    const WorkItem& a = items[i];
+    cost[i] = int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
+  }
+  if (meta_host) xcd_order(sc, n_groups);
+  const std::vector<WorkItem>& ordered = meta_host ? sc.ordered : items;
+  const int32_t n_items = int32_t(ordered.size());
   const MetaLayout lay = meta_layout(batch, n_items, n_split_rows);
   if (meta_bytes_out) *meta_bytes_out = lay.total;
   // key blocks the busiest workgroup slot streams: the longest item, or the
   // average per slot when there are more items than slots
   int64_t max_blocks = 0, sum_blocks = 0;
-  for (const WorkItem& it : items) {
+  for (const WorkItem& it : ordered) {
     const int64_t nb = it.kv_end > it.kv_begin ? ceil_div(it.kv_end, kSplitGranule) - it.kv_begin / kSplitGranule : 0;
     max_blocks = std::max(max_blocks, nb);
     sum_blocks += nb;
@@ -347,7 +395,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       kv[b + 1] = kv[b] + prefix_lens[b] + chunk_lens[b];
       pre[b] = prefix_lens[b];
     }
-    if (n_items) std::memcpy(base + lay.items, items.data(), sizeof(WorkItem) * items.size());
+    if (n_items) std::memcpy(base + lay.items, ordered.data(), sizeof(WorkItem) * ordered.size());
     if (n_split_rows) std::memcpy(base + lay.split_rows, split_rows.data(), sizeof(int32_t) * split_rows.size());
   }
   return PKV_OK;
