@@ -145,10 +145,13 @@ int pkv_extend_metadata_size(int32_t batch, const int32_t* prefix_lens_h, const 
  * device and cached; with no current device (a host-only plan on a machine
  * without a GPU) the plan is sized for an MI355X's 256.
  *   meta_host   caller buffer of >= meta_bytes; it must stay unchanged until
- *               the copy has executed (pinned memory makes the copy async).
- *   meta_dev    device buffer of >= meta_bytes, or NULL for a host-only plan
- *               (then no HIP call is made and the plan's device pointers are
- *               NULL: useful for inspecting the plan without a GPU).
+ *               the copy has executed. Pinned memory (hipHostMalloc) is read
+ *               in place by a small copy kernel on `stream`; other host
+ *               memory goes through hipMemcpyAsync.
+ *   meta_dev    device buffer of >= meta_bytes, 16-byte aligned, or NULL for
+ *               a host-only plan (then no HIP call is made and the plan's
+ *               device pointers are NULL: useful for inspecting the plan
+ *               without a GPU).
  *   plan_out    receives the plan.
  * Errors: PKV_ERR_INVALID_ARGUMENT (null pointers, batch < 1, negative
  * lengths, int32 overflow of the sums, Hq % Hkv != 0, page_size < 1,

@@ -214,10 +214,27 @@ int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const 
   if (meta_dev) {
     if (meta_dev_bytes < total)
       return set_error(PKV_ERR_WORKSPACE, "meta_dev holds %zu bytes, %zu needed", meta_dev_bytes, total);
+    if (reinterpret_cast<uintptr_t>(meta_dev) & 15)
+      return set_error(PKV_ERR_INVALID_ARGUMENT, "meta_dev must be 16-byte aligned");
     if ((st = check_current_device())) return st;
-    const hipError_t e =
-        hipMemcpyAsync(meta_dev, meta_host, total, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return set_error(PKV_ERR_HIP, "metadata copy failed: %s", hipGetErrorString(e));
+    // Pinned meta_host (device-mapped host memory) is copied by a kernel that
+    // reads it in place: one launch at any size, where the runtime's copy of
+    // more than a few KiB goes through the DMA engine and waits for it with a
+    // signal. Other host memory takes the runtime copy.
+    hipPointerAttribute_t attr;
+    const void* src_dev = nullptr;
+    if (hipPointerGetAttributes(&attr, meta_host) == hipSuccess && attr.type == hipMemoryTypeHost &&
+        !(reinterpret_cast<uintptr_t>(attr.devicePointer) & 15))
+      src_dev = attr.devicePointer;
+    else
+      (void)hipGetLastError();   // not memory the runtime knows: leave no error behind
+    if (src_dev) {
+      if ((st = launch_meta_copy(src_dev, meta_dev, total, stream))) return st;
+    } else {
+      const hipError_t e =
+          hipMemcpyAsync(meta_dev, meta_host, total, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return set_error(PKV_ERR_HIP, "metadata copy failed: %s", hipGetErrorString(e));
+    }
     const MetaLayout lay = meta_layout(batch, plan.n_items, plan.n_split_rows);
     char* d = static_cast<char*>(meta_dev);
     plan.qo_indptr = reinterpret_cast<const int32_t*>(d + lay.qo_indptr);

@@ -14,6 +14,8 @@
 // loads are issued before the page lookup so that their latencies overlap.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pkv_internal.hpp"
 
 namespace pkv {
@@ -183,7 +185,25 @@ __global__ __launch_bounds__(1024) void rope_append_kernel(const RopeParams r) {
   }
 }
 
+// Step metadata from the caller's pinned host buffer (read through its device
+// mapping) into meta_dev: 16 bytes per lane, the buffer's size being a
+// multiple of 256 bytes.
+__global__ __launch_bounds__(256) void copy_meta_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        int n16) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n16; i += gridDim.x * 256) dst[i] = src[i];
+}
+
 }  // namespace
+
+int launch_meta_copy(const void* src_dev, void* dst, size_t bytes, void* stream) {
+  const int n16 = int(bytes / 16);
+  const int blocks = std::max(1, std::min(128, (n16 + 255) / 256));
+  hipLaunchKernelGGL(copy_meta_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src_dev), static_cast<uint4*>(dst), n16);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(PKV_ERR_HIP, "metadata copy failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
 
 int launch_append(const AppendArgs& a, void* stream) {
   const int esize = a.shape.dtype == PKV_DTYPE_BF16 ? 2 : 4;

@@ -172,4 +172,8 @@ struct AppendArgs {
 
 int launch_append(const AppendArgs& a, void* stream);
 
+// Copies `bytes` (a multiple of 256) from a device-readable address of pinned
+// host memory to device memory with a kernel (append.hip).
+int launch_meta_copy(const void* src_dev, void* dst, size_t bytes, void* stream);
+
 }  // namespace pkv
