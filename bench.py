@@ -140,8 +140,8 @@ def main():
     ap.add_argument("--workload", default="prompt4097_chunk512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
-                    help="also time the step replayed from captured HIP graphs (append + attention per batch, "
-                         "metadata built once), reported as graph_replay")
+                    help="also time the whole step replayed from one captured HIP graph (every batch's append + "
+                         "attention in order, metadata built once), reported as graph_replay")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows for the CPU oracle sample (0: auto)")
     ap.add_argument("--mask", choices=["none", "rows", "heads"], default="none",
                     help="run paged_extend_attn_masked with an all-keep mask of [B, 1, max_q_len, Ks] (rows) or "
@@ -155,6 +155,8 @@ def main():
                          "of pkv_append) before the attention; reports that kernel's HBM rate")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--stats-json", metavar="PATH", help="with --summarize-stats: also write the attention "
+                    "kernel's average duration and the combine's time per call as JSON (profiles/stats_<workload>.json)")
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="rocprofv3 --pmc output directory (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_INSTS_VALU, SQ_INSTS_MFMA, GRBM_GUI_ACTIVE) of --workload: print the attention kernel's "
@@ -359,6 +361,24 @@ def main():
         roofline["traffic_vs_algorithmic_bytes"] = round(tr["traffic_bytes_per_launch"] / (alg / n_launch), 3)
         roofline["traffic_source"] = f"profiles/traffic_{args.workload}.json"
 
+    st = load_profile("stats", args.workload)
+    if st is not None:
+        # the same figure from the rocprofv3 kernel statistics of this command: the attention kernel
+        # alone, and with the split combine's time per call (the event interval also holds the gap
+        # between the two launches)
+        per = roofline["algorithmic_per_launch"]            # FLOPs (bytes for the one-token rows)
+        scale = 1e9 if decode_bound else 1e12                # -> GB/s or TFLOP/s, the peak's unit
+        k_us, c_us = st["extend_attn_avg_us"], st["combine_us_per_attention_call"]
+
+        def frac(us):
+            return round(per / (us * 1e-6) / scale / roofline["peak"], 4)
+
+        roofline["profile"] = {"extend_attn_avg_us": k_us, "combine_us_per_call": c_us,
+                               "frac_kernel": frac(k_us), "frac_kernel_and_combine": frac(k_us + c_us),
+                               "source": f"profiles/stats_{args.workload}.json"}
+    roofline["frac_source"] = ("HIP events around each attention call: the attention kernel, the split combine "
+                               "after it when the plan has split rows, and the gap between them")
+
     graph_replay = None
     if args.graph:
         graph_replay = time_graph_replay(args, B, lib, flops, tokens)
@@ -405,43 +425,47 @@ def main():
 
 
 def time_graph_replay(args, B, lib, flops, tokens):
-    """The same step with each batch's append + attention captured once into a
-    HIP graph on a stream of its own and replayed; each batch's metadata is
-    built once before capture (a step's plan reused, as by every layer)."""
+    """The whole step captured once into one HIP graph and replayed: every batch
+    in order, each with its append and attention (and split combine), on a
+    stream of its own. Each batch's plan is built once before capture (the
+    host planner and the metadata copy stay outside the replay, as when a
+    step's plan serves every layer). Reports the replayed step's rate next to
+    the eager step's."""
     import torch
     s = torch.cuda.Stream()
     sh = ctypes.c_void_p(s.cuda_stream)
-    graphs = []
+    calls = []
     for b in B:
-        if lib.build_extend_metadata(*b["meta_args"][0]):
+        if lib.build_extend_metadata_ex(*b["meta_args"][0]):
             raise RuntimeError(lib.pkv_last_error().decode())
         ap = b["append_args"][:-1] + (sh,)
         at = b["attn_args"][:-1] + (sh,)
-        torch.cuda.synchronize()
-        app = (lambda: b["append_fn"](*ap)) if b["append_fn"] is not None else (lambda: 0)
-        with torch.cuda.stream(s):       # one eager pass on the capture stream first
-            if app() or b["attn_fn"](*at):
+        calls.append((b["append_fn"], ap, b["attn_fn"], at))
+    torch.cuda.synchronize()
+
+    def step():
+        for app_fn, ap, attn_fn, at in calls:
+            if (app_fn is not None and app_fn(*ap)) or attn_fn(*at):
                 raise RuntimeError(lib.pkv_last_error().decode())
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            if app() or b["attn_fn"](*at):
-                raise RuntimeError(lib.pkv_last_error().decode())
-        graphs.append(g)
+
+    with torch.cuda.stream(s):       # one eager pass on the capture stream first
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
     for _ in range(args.warmup):
-        for g in graphs:
-            g.replay()
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for g in graphs:
-            g.replay()
+        g.replay()
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / args.steps
     return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
-            "tokens_per_s": round(tokens / (ms * 1e-3), 1), "graphs_per_step": len(graphs),
-            "note": "append + attention (+ combine) replayed from one captured graph per batch; the host "
-                    "planner and metadata copy run once, outside the timed region"}
+            "tokens_per_s": round(tokens / (ms * 1e-3), 1), "graphs_per_step": 1, "batches_per_graph": len(calls),
+            "note": "the whole step (every batch's append + attention + combine, in order) replayed from one "
+                    "captured graph; the host planner and metadata copies run once, outside the timed region"}
 
 
 def kernel_hash():
@@ -450,14 +474,19 @@ def kernel_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(name):
-    """Counter traffic recorded for this workload, if it was taken on the current kernel source."""
-    path = os.path.join(PROFILES, f"traffic_{name}.json")
+def load_profile(kind, name):
+    """profiles/<kind>_<workload>.json, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"{kind}_{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tr = json.load(f)
     return tr if tr.get("kernel_source_sha256_16") == kernel_hash() else None
+
+
+def load_traffic(name):
+    """Counter traffic recorded for this workload, if it was taken on the current kernel source."""
+    return load_profile("traffic", name)
 
 
 def _counter_means(directory, match):
@@ -532,6 +561,10 @@ def summarize_mfma(args):
 
 
 def summarize_stats(args):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run; with
+    --stats-json, also the attention kernel's average duration and the split
+    combine's time per attention call as JSON (read back by the bench's
+    roofline while the kernel source hash matches)."""
     import csv
     with open(os.path.join(args.summarize_stats, "run_kernel_stats.csv")) as f:
         rows = list(csv.DictReader(f))
@@ -542,6 +575,19 @@ def summarize_stats(args):
         print(f"| `{name[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
               f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
               f"{float(r['Percentage']):.1f} |")
+    if args.stats_json:
+        attn = [r for r in rows if "extend_attn" in r["Name"]]
+        comb = [r for r in rows if "combine_splits" in r["Name"]]
+        calls = sum(int(r["Calls"]) for r in attn)
+        attn_ns = sum(float(r["TotalDurationNs"]) for r in attn)
+        comb_ns = sum(float(r["TotalDurationNs"]) for r in comb)
+        out = {"workload": args.workload, "kernel_source_sha256_16": kernel_hash(), "attention_calls": calls,
+               "extend_attn_avg_us": round(attn_ns / calls / 1e3, 3),
+               "combine_us_per_attention_call": round(comb_ns / calls / 1e3, 3),
+               "combine_calls": sum(int(r["Calls"]) for r in comb)}
+        with open(args.stats_json, "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
 
 
 def copy_calibration(args):

@@ -101,3 +101,59 @@ def test_graph_replay_matches_eager(name, pool_rows, fused):
         ref = oracle_out(w, oracle_pools(w), dtype=np.float32)
         rep = assert_parity(values_of(out), ref, w.dtype, f"graph {name}")
         print(f"[parity] graph {name}: max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_append"])
+def test_whole_prompt_graph_matches_eager_and_oracle(fused):
+    """A whole chunked prefill in one graph: the 4097-token prompt's nine chunks
+    of at most 512 tokens (each chunk's append, then its attention over the
+    prefix the earlier chunks appended), planned before capture and captured in
+    order into one graph. Every replay equals the eager pass bit for bit, and
+    the outputs match the oracle's full prefill."""
+    w = wl.config3(4097)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    steps = wl.chunked_steps(w, wl.chunk_partition(4097, 512))
+    cache = DeviceCache(w, dev)
+    batches = []
+    for st in steps:
+        plan = pkv.build_extend_metadata(st.prefix_lens, st.chunk_lens, shape_of(st), 0, 0, device=dev)
+        kn, vn = cache._gather_new_kv(st)
+        q = upload_q(st, dev)
+        batches.append((plan, kn, vn, q, torch.empty_like(q), plan.workspace()))
+    print(f"[graph] whole prompt, {len(batches)} chunks, fused={fused}", flush=True)
+
+    def path():
+        for plan, kn, vn, q, out, ws in batches:
+            if fused:
+                pkv.paged_extend_attn_append(q, kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out,
+                                             workspace=ws)
+            else:
+                pkv.pkv_append(kn, vn, cache.k_pool, cache.v_pool, cache.page_table, plan)
+                pkv.paged_extend_attn(q, cache.k_pool, cache.v_pool, cache.page_table, plan, out=out, workspace=ws)
+
+    path()
+    torch.cuda.synchronize()
+    eager = torch.cat([b[4] for b in batches]).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    scratch = torch.randn(1 << 20, device=dev)
+    for r in range(3):
+        for b in batches:
+            b[4].fill_(float("nan"))
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = torch.cat([b[4] for b in batches])
+        assert torch.equal(got, eager), f"replay {r} differs from the eager result"
+    assert all(pkv.read_status(b[0]) == 0 for b in batches)
+    ref = oracle_out(w, oracle_pools(w), dtype=np.float32)
+    rep = assert_parity(values_of(eager), ref, "bf16", "whole-prompt graph")
+    print(f"[parity] whole-prompt graph fused={fused}: max_abs={rep['max_abs']:.3e}", flush=True)
