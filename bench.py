@@ -436,7 +436,7 @@ def time_graph_replay(args, B, lib, flops, tokens):
     sh = ctypes.c_void_p(s.cuda_stream)
     calls = []
     for b in B:
-        if lib.build_extend_metadata_ex(*b["meta_args"][0]):
+        if lib.build_extend_metadata(*b["meta_args"][0]):
             raise RuntimeError(lib.pkv_last_error().decode())
         ap = b["append_args"][:-1] + (sh,)
         at = b["attn_args"][:-1] + (sh,)

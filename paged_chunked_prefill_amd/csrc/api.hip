@@ -66,6 +66,10 @@ int current_device_cus() {
 
 constexpr int32_t kMaxPlanCUs = 65536;
 
+// Largest host-to-device copy the HIP runtime makes with a kernel of its own
+// (beyond it, the DMA engine).
+constexpr size_t kRuntimeKernelCopyBytes = 16 << 10;
+
 int resolve_cus(int32_t num_cus, int32_t* out) {
   if (num_cus < 0 || num_cus > kMaxPlanCUs)
     return set_error(PKV_ERR_INVALID_ARGUMENT, "num_cus must be in 0..%d (got %d)", kMaxPlanCUs, num_cus);
@@ -217,17 +221,20 @@ int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const 
     if (reinterpret_cast<uintptr_t>(meta_dev) & 15)
       return set_error(PKV_ERR_INVALID_ARGUMENT, "meta_dev must be 16-byte aligned");
     if ((st = check_current_device())) return st;
-    // Pinned meta_host (device-mapped host memory) is copied by a kernel that
-    // reads it in place: one launch at any size, where the runtime's copy of
-    // more than a few KiB goes through the DMA engine and waits for it with a
-    // signal. Other host memory takes the runtime copy.
+    // The runtime copies up to 16 KiB from pinned memory with a copy kernel of
+    // its own (2.7 us); above that it takes the DMA engine, and the next kernel
+    // then starts 9-34 us after the copy ends. Larger pinned meta_host
+    // (device-mapped host memory) is copied by a kernel that reads it in
+    // place: one launch at any size. Other host memory takes the runtime copy.
     hipPointerAttribute_t attr;
     const void* src_dev = nullptr;
-    if (hipPointerGetAttributes(&attr, meta_host) == hipSuccess && attr.type == hipMemoryTypeHost &&
-        !(reinterpret_cast<uintptr_t>(attr.devicePointer) & 15))
-      src_dev = attr.devicePointer;
-    else
-      (void)hipGetLastError();   // not memory the runtime knows: leave no error behind
+    if (total > kRuntimeKernelCopyBytes) {
+      if (hipPointerGetAttributes(&attr, meta_host) == hipSuccess && attr.type == hipMemoryTypeHost &&
+          !(reinterpret_cast<uintptr_t>(attr.devicePointer) & 15))
+        src_dev = attr.devicePointer;
+      else
+        (void)hipGetLastError();   // not memory the runtime knows: leave no error behind
+    }
     if (src_dev) {
       if ((st = launch_meta_copy(src_dev, meta_dev, total, stream))) return st;
     } else {
