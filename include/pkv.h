@@ -36,6 +36,9 @@
  *                         NULL. Only entries of positions < N_b are read.
  *     Tokens of the batch are in request order: request b owns q/out/k_new/
  *     v_new rows qo_indptr[b] .. qo_indptr[b+1]-1.
+ *     q, out, k_new, v_new, the pools, q_out, rope_table and the workspace
+ *     must be 16-byte aligned (the kernels move 16-byte vectors); a
+ *     misaligned one is PKV_ERR_INVALID_ARGUMENT.
  *   - Element type: bf16 (round-to-nearest-even outputs, fp32 accumulation)
  *     or fp32, chosen by pkv_shape.dtype for all of q, pools, out.
  *   - Page ids read from the page table outside [0, num_pages) are never

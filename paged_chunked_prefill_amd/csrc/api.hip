@@ -255,6 +255,9 @@ int build_extend_metadata_ex(int32_t batch, const int32_t* prefix_lens_h, const 
   return PKV_OK;
 }
 
+// Every kernel moves 16-byte vectors of these tensors.
+static bool misaligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+
 int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* page_table,
                int32_t page_table_stride, const int32_t* req_pool_indices, const pkv_plan* plan,
                const pkv_shape* shape, pkv_stream_t stream) {
@@ -264,6 +267,8 @@ int pkv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
   if ((st = check_page_table(page_table, page_table_stride, plan, "pkv_append"))) return st;
   if (plan->total_q > 0 && (!k_new || !v_new || !k_pool || !v_pool))
     return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_append: K/V pointers must not be NULL");
+  if (plan->total_q > 0 && (misaligned16(k_new) || misaligned16(v_new) || misaligned16(k_pool) || misaligned16(v_pool)))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_append: K/V pointers must be 16-byte aligned");
   if ((st = check_current_device())) return st;
   AppendArgs a;
   a.k_new = k_new;
@@ -292,8 +297,10 @@ int pkv_rope_append(const void* q, void* q_out, const void* k_new, const void* v
   if ((st = check_page_table(page_table, page_table_stride, plan, "pkv_rope_append"))) return st;
   if (plan->total_q > 0 && (!q || !q_out || !k_new || !v_new || !k_pool || !v_pool || !rope_table))
     return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_rope_append: q, q_out, K/V, pools and rope_table must not be NULL");
-  if (rope_table && (reinterpret_cast<uintptr_t>(rope_table) & 15))
-    return set_error(PKV_ERR_INVALID_ARGUMENT, "pkv_rope_append: rope_table must be 16-byte aligned");
+  if (plan->total_q > 0 && (misaligned16(q) || misaligned16(q_out) || misaligned16(k_new) || misaligned16(v_new) ||
+                            misaligned16(k_pool) || misaligned16(v_pool) || misaligned16(rope_table)))
+    return set_error(PKV_ERR_INVALID_ARGUMENT,
+                     "pkv_rope_append: q, q_out, K/V, pools and rope_table must be 16-byte aligned");
   if (plan->total_q > 0 && rope_table_len < plan->max_kv_len)
     return set_error(PKV_ERR_INVALID_ARGUMENT,
                      "pkv_rope_append: rope_table has %d positions, the batch reaches position %d", rope_table_len,
@@ -336,6 +343,10 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
                      plan->window);
   if (plan->total_q > 0 && (!q || !k_pool || !v_pool || !out))
     return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: q, pools and out must not be NULL", name);
+  if (plan->total_q > 0 && (misaligned16(q) || misaligned16(k_pool) || misaligned16(v_pool) || misaligned16(out) ||
+                            misaligned16(workspace) || misaligned16(k_new) || misaligned16(v_new)))
+    return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: q, pools, out, workspace and new K/V must be 16-byte aligned",
+                     name);
   if (!(std::isfinite(sm_scale)))
     return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: sm_scale is not finite", name);
   // the batch arrays: NULL or the plan's own device copies (the kernels take

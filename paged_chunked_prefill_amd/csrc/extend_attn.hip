@@ -49,6 +49,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -758,39 +759,63 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
 
   if (!wave_live) return;
   const float l_tot = other_half_sum(l_run);
-  if (!row_live) return;
-  // O^T accumulator: register j of block db is d = 32db + 8(j/4) + 4half + j%4 of this lane's row
-  if (it.part_row < 0) {
-    // divide (not multiply by a reciprocal): exact whenever the quotient is representable
-    const float den = l_tot > 0.f ? l_tot : INFINITY;
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + (int64_t(gtok) * p.num_q_heads + head) * D;
+  const bool split_item = it.part_row >= 0;
+  if (split_item && row_live && half == 0) {
+    // reference max (log2 units) the partial is relative to, and its sum
+    const int64_t prow = (int64_t(it.part_row + tok) * p.num_q_heads + head) * p.max_splits + it.split;
+    *reinterpret_cast<f32x2*>(p.ml_part + prow * 2) = f32x2{m_ref, l_tot};
+  }
+  // The wave's 32 x D tile -- the output (O / l, l = 0 giving 0) or the split's
+  // unnormalised partial, both bf16 -- goes out through LDS: written in the
+  // accumulator's layout (register j of block db is d = 32db + 8(j/4) + 4half +
+  // j%4 of the lane's row), read back as whole rows, so that a store instruction
+  // writes RPI complete rows instead of 8 bytes of each of 32 rows. It is staged
+  // in the wave's own rows of the stages of tiles ntiles+1 and ntiles+2: rows
+  // that only this wave's copies write (they have landed, waited for above) and
+  // that no wave reads again (they hold no tile of the item), so no other wave is
+  // waited for. Piece g (tile rows RPI g .. RPI g + RPI-1) takes the rows of copy
+  // g % LOADS, K tile for (g / LOADS) even, V tile for odd, of the first stage for
+  // g < 2 LOADS, of the second for the rest; chunks are XOR-swizzled by row like
+  // the K tiles.
+  const float scale_out = split_item ? 1.f : (l_tot > 0.f ? 1.f / l_tot : 0.f);
+  constexpr int PIECES = 32 / T::RPI;
+  static_assert(PIECES == 4 * T::LOADS, "a wave's tile fills its rows of two stages");
+  auto piece_base = [&](int g) __attribute__((always_inline)) {
+    const uint32_t stage = stage_of(ntiles + 1 + (g >= 2 * T::LOADS ? 1 : 0)) - lds0;
+    return stage + uint32_t(((g / T::LOADS) & 1) * T::TILEB) +
+           uint32_t(T::RPI * (T::NW * (g % T::LOADS) + wave) * T::ROWB);
+  };
+  {
+    const uint32_t wrow = piece_base(l32 / T::RPI) + uint32_t(l32 % T::RPI) * T::ROWB;
 #pragma unroll
     for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         bf16x4 v;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = (__bf16)(o[db][4 * jj + x] / den);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jj + 4 * half) = __builtin_bit_cast(u32x2, v);
+        for (int x = 0; x < 4; ++x) v[x] = (__bf16)(o[db][4 * jj + x] * scale_out);
+        const int chunk = (4 * db + jj) ^ T::kswz(l32);
+        *reinterpret_cast<u32x2*>(smem + wrow + 16 * chunk + 8 * half) = __builtin_bit_cast(u32x2, v);
       }
-  } else {
-    const int64_t slot = int64_t(it.part_row + tok) * p.num_q_heads + head;
-    const int64_t prow = slot * p.max_splits + it.split;
-    // unnormalised partial in bf16: one more rounding of the output's own size
-    uint16_t* op = static_cast<uint16_t*>(p.o_part) + prow * D;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back by other lanes
+  const int ec = lane % T::CH;
+  // token = row / G for rows < 256 and G <= 128: (row * ceil(2^16 / G)) >> 16 is exact
+  const uint32_t inv_g = (65536u + uint32_t(G) - 1) / uint32_t(G);
 #pragma unroll
-    for (int db = 0; db < T::DBLK; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 v;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = (__bf16)o[db][4 * jj + x];
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj + 4 * half) = __builtin_bit_cast(u32x2, v);
-      }
-    if (half == 0) {
-      p.ml_part[prow * 2] = m_ref;   // reference max (log2 units) the partial is relative to
-      p.ml_part[prow * 2 + 1] = l_tot;
-    }
+  for (int g = 0; g < PIECES; ++g) {
+    const int er = T::RPI * g + lane / T::CH;   // row within the wave's tile
+    const u32x4 val =
+        *reinterpret_cast<const u32x4*>(smem + piece_base(g) + (lane / T::CH) * T::ROWB + 16 * (ec ^ T::kswz(er)));
+    const int rr = wave * 32 + er;              // tile row = token * G + head-in-group
+    const int etok = int((uint32_t(rr) * inv_g) >> 16);
+    const int ehead = it.kv_head * G + (rr - etok * G);
+    if (etok >= it.q_count || it.tok0 + etok >= p.total_q) continue;
+    uint16_t* dst = split_item
+        ? static_cast<uint16_t*>(p.o_part) +
+              ((int64_t(it.part_row + etok) * p.num_q_heads + ehead) * p.max_splits + it.split) * D
+        : static_cast<uint16_t*>(p.out) + (int64_t(it.tok0 + etok) * p.num_q_heads + ehead) * D;
+    *reinterpret_cast<u32x4*>(dst + 8 * ec) = val;
   }
 }
 

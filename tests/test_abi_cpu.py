@@ -465,6 +465,36 @@ def test_batch_arrays_must_be_the_plans_own():
             assert "device" in lib.pkv_last_error().decode()
 
 
+def test_misaligned_tensors_are_refused():
+    """Every kernel moves 16-byte vectors: a q, pool, out, workspace or new-K/V
+    pointer that is not 16-byte aligned is refused before any HIP call.
+    (Stand-in device pointers: nothing runs.)"""
+    lib = pkv.lib()
+    s = shape()
+    p = pkv.build_extend_metadata([3], [2], s)
+    fake = p.plan
+    fake.qo_indptr, fake.kv_indptr, fake.prefix_lens, fake.items, fake.status = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    d, bad = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+
+    def attn(q=d, k=d, v=d, out=d):
+        return lib.paged_extend_attn(q, k, v, d, 4, None, None, None, None, 0, 0.0, ctypes.byref(fake),
+                                     ctypes.byref(s), out, None, 0, None)
+
+    for kw in ({"q": bad}, {"k": bad}, {"v": bad}, {"out": bad}):
+        assert attn(**kw) == pkv.PKV_ERR_INVALID_ARGUMENT
+        assert "16-byte aligned" in lib.pkv_last_error().decode()
+    assert attn() == pkv.PKV_ERR_HIP   # aligned: stops at the device check (no GPU here)
+    kn, vn, kp, vp_ = (ctypes.c_void_p(a) for a in (0x100008, 0x200000, 0x1000000, 0x2000000))
+    st = lib.paged_extend_attn_append(d, kn, vn, kp, vp_, d, 4, None, 0, 0.0, ctypes.byref(fake), ctypes.byref(s),
+                                      d, None, 0, None)
+    assert st == pkv.PKV_ERR_INVALID_ARGUMENT and "16-byte aligned" in lib.pkv_last_error().decode()
+    for args in ((bad, d, d, d), (d, d, d, bad)):
+        assert lib.pkv_append(*args, d, 4, None, ctypes.byref(fake), ctypes.byref(s), None) == pkv.PKV_ERR_INVALID_ARGUMENT
+        assert "16-byte aligned" in lib.pkv_last_error().decode()
+    st = lib.pkv_rope_append(d, bad, d, d, d, 64, d, d, d, 4, None, ctypes.byref(fake), ctypes.byref(s), None)
+    assert st == pkv.PKV_ERR_INVALID_ARGUMENT and "16-byte aligned" in lib.pkv_last_error().decode()
+
+
 def test_noalloc_refuses_plans_beyond_its_scratch():
     """paged_extend_attn_noalloc: a plan whose split partials exceed the static
     scratch is refused with PKV_ERR_WORKSPACE before any HIP call; a NULL plan
