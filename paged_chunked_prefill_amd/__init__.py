@@ -79,7 +79,8 @@ WORK_ITEM_DTYPE = np.dtype([("req", "<i4"), ("head_split", "<i4"), ("tok0", "<i4
                             ("q_count", "<i4"), ("kv_begin", "<i4"), ("kv_end", "<i4"), ("part_row", "<i4")])
 SPLIT_BITS = 8
 # Decoded view: the packed fields plus KV head, split and the tile's first chunk token.
-WORK_ITEM_VIEW = np.dtype(WORK_ITEM_DTYPE.descr + [("kv_head", "<i4"), ("split", "<i4"), ("q_begin", "<i4")])
+WORK_ITEM_VIEW = np.dtype(WORK_ITEM_DTYPE.descr + [("kv_head", "<i4"), ("split", "<i4"), ("q_begin", "<i4"),
+                                                  ("position", "<i4")])
 
 
 def extend_metadata_size(prefix_lens, chunk_lens, shape: PkvShape, window: int = 0, decode_splits: int = 0,
@@ -129,13 +130,20 @@ class ExtendPlan:
             out[name] = raw[off:off + nbytes].view(dt).copy()
             off = _align256(off + nbytes)
         out["split_rows"] = out["split_rows"].reshape(-1, 2)
-        raw_items, items = out["items"], np.zeros(ni, WORK_ITEM_VIEW)
+        # "items": the work items in dispatch order ("position" = workgroup index);
+        # "padding": the empty items (q_count 0) that even out the XCD lists of a
+        # stream plan, which the kernels skip
+        raw_all = out["items"]
+        real = raw_all["q_count"] > 0
+        raw_items, items = raw_all[real], np.zeros(int(real.sum()), WORK_ITEM_VIEW)
         for f in WORK_ITEM_DTYPE.names:
             items[f] = raw_items[f]
         items["kv_head"] = raw_items["head_split"] >> (2 * SPLIT_BITS)
         items["split"] = raw_items["head_split"] & ((1 << SPLIT_BITS) - 1)
         items["q_begin"] = raw_items["tok0"] - out["qo_indptr"][raw_items["req"]]
+        items["position"] = np.nonzero(real)[0]
         out["items"] = items
+        out["padding"] = raw_all[~real]
         return out
 
 

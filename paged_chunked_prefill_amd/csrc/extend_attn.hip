@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char*)smem));
 
   const ItemView it = load_item(p);
-  if (it.q_count <= 0) return;   // (uniform) a malformed item covers no row
+  if (it.q_count <= 0) return;   // (uniform) a padding item covers no row
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -843,6 +843,7 @@ __global__ __launch_bounds__(256) void extend_attn_f32(const Params p) {
   __shared__ float smem[2 * T::STAGE];
 
   const ItemView it = load_item(p);
+  if (it.q_count <= 0) return;   // (uniform) a padding item covers no row
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int G = p.group;

@@ -49,7 +49,7 @@ struct alignas(16) WorkItem {
   int32_t head_split;  // KV head hk << 16 | the tile's split count S << 8 | split index k (S = 1, k = 0 unsplit)
   int32_t tok0;        // global token index of the tile's first token: qo_indptr[b] + first chunk token
   int32_t pos0;        // its absolute position: P_b + first chunk token
-  int32_t q_count;     // tokens in the tile (>= 1, all inside the chunk)
+  int32_t q_count;     // tokens in the tile (all inside the chunk); 0: a padding item, skipped
   int32_t kv_begin;    // first key position this item covers
   int32_t kv_end;      // one past the last key position (<= N_b)
   int32_t part_row;    // -1: write `out`; else partial slot of the tile's first token

@@ -59,16 +59,56 @@ struct Tile {
 
 int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
 
+// Predicted time of one bf16 work item on MI355X, in ns (per-workgroup
+// timestamps of the attention kernel): about 5.6 us of its own (the Q rows and
+// the first K/V tiles into LDS, the first scores, the output stores; more for
+// the first workgroup on each compute unit, the same for every plan), then
+// 1390 + 67 w ns per 64-key block for w live 32-row waves. A split item also costs about 26 ns of
+// HBM time for its partial rows (256 rows of D values and (max, sum), written
+// and read back by the combine).
+constexpr int64_t kItemNs = 5600;
+constexpr int64_t kBlockNs = 1390;
+constexpr int64_t kBlockWaveNs = 67;
+constexpr int64_t kPartialNs = 26;
+// Cap on the pieces of one tile in a stream plan (its split count).
+constexpr int32_t kMaxStreamSplits = 32;
+// Within an XCD, workgroups go to its 4 shader engines in turn -- the XCD's
+// j-th workgroup to engine class j mod 4 -- strictly in order: a workgroup
+// waits for a free compute unit of its engine and holds back every later one
+// of its XCD (per-workgroup hardware ids and timestamps on MI355X).
+constexpr int kSeClasses = 4;
+
+// One piece of a stream plan: 64-key blocks [g0, g1) of a tile, in run `run`,
+// starting `start` ns after the run's first piece.
+struct Piece {
+  int32_t tile, g0, g1, run;
+  int64_t start;
+};
+// A stream-plan item placed for dispatch: XCD, shader-engine class, whether it
+// is its run's first piece (0) or a later one (1), its predicted start within
+// its run (later pieces), its duration, and its index in the item list.
+struct Placed {
+  int32_t xcd, cls, later;
+  int64_t key, dur;
+  int32_t seq;
+};
+
 // The planner's buffers, kept per thread and reused from call to call: after a
 // thread's first few plans no call allocates.
 struct Scratch {
   std::vector<Tile> tiles;
-  std::vector<int32_t> qo_start, tile_splits, req_splits, group_base, gid, split_rows, xcd_count, xcd_start;
+  std::vector<int32_t> qo_start, tile_splits, tile_part, req_splits, group_base, gid, xcd_count, xcd_start;
   std::vector<WorkItem> items, ordered;
   std::vector<int64_t> cost, group_cost;
   std::vector<uint64_t> packed, gpacked;
   std::vector<uint8_t> xcd_of;
   std::vector<uint32_t> by_xcd;
+  // stream plan
+  std::vector<int64_t> block_ns, run_load;
+  std::vector<int32_t> piece_count, piece_next;
+  std::vector<Piece> pieces;
+  std::vector<Placed> placed;
+  std::vector<int32_t> run_first, run_cls;
 };
 
 Scratch& scratch() {
@@ -140,6 +180,36 @@ void xcd_order(Scratch& sc, int32_t ng) {
     }
     out.push_back(in[sc.by_xcd[size_t(start[x] + next[x]++)]]);
   }
+}
+
+// Stream cut: one KV head's work -- each tile's 64-key blocks [g0(t), g1(t)),
+// tiles in order -- laid end to end and cut into runs of predicted time <= T
+// (ns), each piece (the blocks of one tile inside one run) charged a
+// prologue. Returns the runs used, or limit + 1 as soon as more are needed or
+// a tile would get more than kMaxStreamSplits pieces. T must fit a prologue
+// and one block of every tile.
+int32_t stream_cut(const std::vector<Tile>& tiles, Scratch& sc, int64_t T, int32_t limit, bool keep) {
+  sc.piece_count.assign(tiles.size(), 0);
+  if (keep) sc.pieces.clear();
+  int32_t runs = 0;
+  int64_t room = -1;
+  for (size_t t = 0; t < tiles.size(); ++t) {
+    const int64_t bns = sc.block_ns[t];
+    int32_t g = tiles[t].kv_lo / kSplitGranule;
+    const int32_t ge = g + std::max(1, ceil_div(tiles[t].kv_hi, kSplitGranule) - g);
+    while (g < ge) {
+      if (room < kItemNs + bns) {
+        if (++runs > limit) return limit + 1;
+        room = T;
+      }
+      const int32_t take = int32_t(std::min<int64_t>(ge - g, (room - kItemNs) / bns));
+      if (++sc.piece_count[t] > kMaxStreamSplits) return limit + 1;
+      if (keep) sc.pieces.push_back(Piece{int32_t(t), g, g + take, runs - 1, T - room});
+      room -= kItemNs + take * bns;
+      g += take;
+    }
+  }
+  return runs;
 }
 
 }  // namespace
@@ -283,55 +353,253 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     n_groups += hkv * req_splits[size_t(b)];
   }
 
-  std::vector<WorkItem>& items = sc.items;
-  items.clear();
-  items.reserve(size_t(n_alloc));
-  std::vector<int32_t>& gid = sc.gid;
-  gid.clear();
-  gid.reserve(size_t(n_alloc));
-  std::vector<int32_t>& split_rows = sc.split_rows;  // pairs (token, splits)
-  split_rows.clear();
+  // each split tile's partial rows (tile_part; -1 when unsplit): one per token
+  std::vector<int32_t>& tile_part = sc.tile_part;
+  tile_part.resize(tiles.size());
   int32_t n_split_rows = 0, max_splits = 1;
-  for (size_t ti = 0; ti < tiles.size(); ++ti) {
-    const Tile& t = tiles[ti];
-    const int32_t g0 = t.kv_lo / kSplitGranule;
-    const int32_t granules = granules_of(t);
-    const int32_t splits = tile_splits[ti];
-    int32_t part_row = -1;
-    if (splits > 1) {
-      part_row = n_split_rows;
-      n_split_rows += t.q_count;
-      max_splits = std::max(max_splits, splits);
+  auto number_split_rows = [&]() {
+    n_split_rows = 0;
+    max_splits = 1;
+    for (size_t ti = 0; ti < tiles.size(); ++ti) {
+      tile_part[ti] = -1;
+      if (tile_splits[ti] > 1) {
+        tile_part[ti] = n_split_rows;
+        n_split_rows += tiles[ti].q_count;
+        max_splits = std::max(max_splits, tile_splits[ti]);
+      }
     }
-    const int32_t rs = req_splits[size_t(t.req)], gb = group_base[size_t(t.req)];
-    for (int32_t h = 0; h < hkv; ++h) {
-      for (int32_t k = 0; k < splits; ++k) {
-        WorkItem it;
-        it.req = t.req;
-        it.head_split = (h << (2 * kSplitBits)) | (splits << kSplitBits) | k;
-        it.tok0 = qo_start[t.req] + t.q_begin;
-        it.pos0 = causal ? prefix_lens[t.req] + t.q_begin : kNonCausalPos;
-        it.q_count = t.q_count;
-        if (splits == 1) {
-          it.kv_begin = t.kv_lo;
-          it.kv_end = t.kv_hi;
-        } else {
-          const int32_t ga = g0 + int32_t(int64_t(k) * granules / splits);
-          const int32_t gbk = g0 + int32_t(int64_t(k + 1) * granules / splits);
-          it.kv_begin = std::max(t.kv_lo, ga * kSplitGranule);
-          it.kv_end = std::min(t.kv_hi, gbk * kSplitGranule);
+  };
+  number_split_rows();
+
+  std::vector<WorkItem>& items = sc.items;
+  items.resize(size_t(n_alloc));
+  std::vector<int32_t>& gid = sc.gid;
+  gid.resize(size_t(n_alloc));
+  {
+    WorkItem* out = items.data();
+    int32_t* out_gid = gid.data();
+    for (size_t ti = 0; ti < tiles.size(); ++ti) {
+      const Tile& t = tiles[ti];
+      const int32_t g0 = t.kv_lo / kSplitGranule;
+      const int32_t granules = granules_of(t);
+      const int32_t splits = tile_splits[ti];
+      const int32_t rs = req_splits[size_t(t.req)], gb = group_base[size_t(t.req)];
+      WorkItem it;
+      it.req = t.req;
+      it.tok0 = qo_start[size_t(t.req)] + t.q_begin;
+      it.pos0 = causal ? prefix_lens[t.req] + t.q_begin : kNonCausalPos;
+      it.q_count = t.q_count;
+      it.part_row = tile_part[ti];
+      for (int32_t h = 0; h < hkv; ++h) {
+        for (int32_t k = 0; k < splits; ++k) {
+          it.head_split = (h << (2 * kSplitBits)) | (splits << kSplitBits) | k;
+          if (splits == 1) {
+            it.kv_begin = t.kv_lo;
+            it.kv_end = t.kv_hi;
+          } else {
+            const int32_t ga = g0 + int32_t(int64_t(k) * granules / splits);
+            const int32_t gbk = g0 + int32_t(int64_t(k + 1) * granules / splits);
+            it.kv_begin = std::max(t.kv_lo, ga * kSplitGranule);
+            it.kv_end = std::min(t.kv_hi, gbk * kSplitGranule);
+          }
+          *out++ = it;
+          *out_gid++ = gb + h * rs + k;
         }
-        it.part_row = part_row;
-        items.push_back(it);
-        gid.push_back(gb + h * rs + k);
       }
     }
-    if (splits > 1) {
-      // token indices are global: qo_indptr[req] + q_begin + i
-      for (int32_t i = 0; i < t.q_count; ++i) {
-        split_rows.push_back(qo_start[t.req] + t.q_begin + i);
-        split_rows.push_back(splits);
+  }
+
+  // ---- Stream plan. Equal cuts of each tile, one item per slot, leave the
+  // slots as uneven as the tiles (a causal chunk's later tiles see more keys).
+  // The alternative: one KV head's tiles cut end to end into runs of nearly
+  // equal predicted time (stream_cut), one run per slot, every KV head cut
+  // alike on its own share of the slots (the combine takes one split count per
+  // token), the runs spread evenly over the XCDs with each head's runs on
+  // neighbouring ones. A run of several pieces relies on how the hardware
+  // hands out workgroups (kSeClasses): each shader engine's next workgroup
+  // goes to the first of its compute units that frees up, so each engine
+  // class gets runs of similar first pieces and its later pieces in the order
+  // of their predicted start, and shorter class lists are padded with empty
+  // items. Taken when its predicted time, partials included, is at least 1/32
+  // below the plan above; only for bf16 lists with prefill tiles, automatic
+  // splits and at most one item per slot.
+  bool streamed = false;
+  int64_t stream_blocks = 0;
+  const int64_t runs_per_head = slots / hkv;
+  std::vector<WorkItem>& ordered_out = sc.ordered;
+  if (shape->dtype == PKV_DTYPE_BF16 && decode_splits == 0 && n_one < int32_t(tiles.size()) && runs_per_head >= 1 &&
+      int64_t(items.size()) <= slots) {
+    // the plan above: its longest item (one per slot) and its partials
+    int64_t cur_max = 0, cur_split = 0;
+    for (const WorkItem& a : items) {
+      const int64_t nb = a.kv_end > a.kv_begin ? ceil_div(a.kv_end, kSplitGranule) - a.kv_begin / kSplitGranule : 0;
+      const int64_t w = std::min<int64_t>(8, (int64_t(a.q_count) * group + 31) / 32);
+      cur_max = std::max(cur_max, kItemNs + nb * (kBlockNs + kBlockWaveNs * w));
+      cur_split += a.part_row >= 0;
+    }
+    const int64_t cur_cost = cur_max + kPartialNs * cur_split;
+    // Run time bounds: at least a piece of one block, and at least the block
+    // work over the runs plus a prologue (every run has one); a greedy cut at
+    // the work over the runs plus one prologue per tile over the runs, two more
+    // prologues and a block always fits (a run leaves less than a prologue and
+    // a block unused, and a cut adds one prologue).
+    sc.block_ns.resize(tiles.size());
+    int64_t piece_min = 0, work = 0, block_max = 0;
+    for (size_t t = 0; t < tiles.size(); ++t) {
+      sc.block_ns[t] = kBlockNs + kBlockWaveNs * std::min<int64_t>(8, waves_of(tiles[t]));
+      piece_min = std::max(piece_min, kItemNs + sc.block_ns[t]);
+      block_max = std::max(block_max, sc.block_ns[t]);
+      work += int64_t(granules_of(tiles[t])) * sc.block_ns[t];
+    }
+    const int64_t total = work + int64_t(tiles.size()) * kItemNs;   // everything in one run
+    const int32_t limit = int32_t(std::min<int64_t>(runs_per_head, INT32_MAX - 1));
+    int64_t lo = std::max(piece_min, (work + limit - 1) / limit + kItemNs);
+    int64_t hi = std::min(total, (total + limit - 1) / limit + 2 * kItemNs + block_max);
+    lo = std::min(lo, hi);
+    // no cut can beat the plan above by 1/32 when even the bound cannot (a
+    // near-even plan): skip the search
+    if (lo + lo / 32 >= cur_cost) hi = lo = -1;
+    else if (stream_cut(tiles, sc, hi, limit, false) > limit) hi = total;   // only the split cap can get here
+    // the shortest run time (to within 1/256) whose cut fits
+    while (hi > 0 && hi - lo > std::max<int64_t>(64, hi / 256)) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (stream_cut(tiles, sc, mid, limit, false) <= limit) hi = mid; else lo = mid + 1;
+    }
+    const int32_t runs = hi > 0 ? stream_cut(tiles, sc, hi, limit, true) : 0;
+    sc.run_load.assign(size_t(runs), 0);
+    std::vector<int64_t>& run_blocks = sc.cost;   // (free until the dispatch order below)
+    run_blocks.assign(size_t(runs), 0);
+    for (const Piece& pc : sc.pieces) {
+      sc.run_load[size_t(pc.run)] += kItemNs + int64_t(pc.g1 - pc.g0) * sc.block_ns[size_t(pc.tile)];
+      run_blocks[size_t(pc.run)] += pc.g1 - pc.g0;
+    }
+    int64_t split_pieces = 0;
+    for (int32_t c : sc.piece_count) split_pieces += c > 1 ? c : 0;
+    const int64_t stream_cost =
+        runs > 0 ? *std::max_element(sc.run_load.begin(), sc.run_load.end()) + kPartialNs * hkv * split_pieces : 0;
+    if (runs > 0 && stream_cost + stream_cost / 32 < cur_cost) {
+      streamed = true;
+      stream_blocks = *std::max_element(run_blocks.begin(), run_blocks.end());
+      // split counts: the tiles' pieces
+      for (size_t t = 0; t < tiles.size(); ++t) tile_splits[t] = sc.piece_count[t];
+      number_split_rows();
+      // split index of each piece (a tile's pieces come in key order) and each
+      // run's first piece (a run's pieces are consecutive)
+      const size_t np = sc.pieces.size();
+      sc.piece_next.assign(tiles.size(), 0);
+      gid.resize(np);
+      sc.run_first.assign(size_t(runs) + 1, 0);
+      for (size_t i = 0; i < np; ++i) {
+        gid[i] = sc.piece_next[size_t(sc.pieces[i].tile)]++;
+        ++sc.run_first[size_t(sc.pieces[i].run) + 1];
       }
+      for (int32_t r = 0; r < runs; ++r) sc.run_first[size_t(r) + 1] += sc.run_first[size_t(r)];
+      // runs by the length of their first piece (the same for every KV head)
+      sc.packed.resize(size_t(runs));
+      for (int32_t r = 0; r < runs; ++r) {
+        const Piece& f = sc.pieces[size_t(sc.run_first[size_t(r)])];
+        sc.packed[size_t(r)] = (uint64_t(f.g1 - f.g0) * uint64_t(sc.block_ns[size_t(f.tile)]) << 20) | uint64_t(r);
+      }
+      std::sort(sc.packed.begin(), sc.packed.end());
+      // (head, run) -> XCD; per XCD the runs in that order are dealt to the
+      // engine classes in turn (rank mod kSeClasses), heads one after another
+      const int64_t total_runs = int64_t(runs) * hkv;   // <= slots: at most slots / 8 runs per XCD
+      auto xcd_of_run = [&](int32_t h, int32_t r) { return int32_t((int64_t(h) * runs + r) * kXcds / total_runs); };
+      sc.run_cls.assign(size_t(total_runs), 0);
+      int32_t rank[kXcds] = {};
+      for (int32_t h = 0; h < hkv; ++h)
+        for (uint64_t pk : sc.packed) {
+          const int32_t r = int32_t(pk & 0xfffff);
+          sc.run_cls[size_t(h) * size_t(runs) + size_t(r)] = rank[xcd_of_run(h, r)]++ % kSeClasses;
+        }
+      // items, then (XCD, class) buckets: the first pieces in the dealing
+      // order above, then the later pieces by predicted start
+      auto make_item = [&](int32_t h, size_t i) {
+        const Piece& pc = sc.pieces[i];
+        const Tile& tl = tiles[size_t(pc.tile)];
+        const int32_t S = sc.piece_count[size_t(pc.tile)];
+        WorkItem it;
+        it.req = tl.req;
+        it.head_split = (h << (2 * kSplitBits)) | (S << kSplitBits) | gid[i];
+        it.tok0 = qo_start[size_t(tl.req)] + tl.q_begin;
+        it.pos0 = causal ? prefix_lens[tl.req] + tl.q_begin : kNonCausalPos;
+        it.q_count = tl.q_count;
+        it.kv_begin = std::max(tl.kv_lo, pc.g0 * kSplitGranule);
+        it.kv_end = std::min(tl.kv_hi, pc.g1 * kSplitGranule);
+        it.part_row = tile_part[size_t(pc.tile)];
+        return it;
+      };
+      int32_t cnt[kXcds][kSeClasses] = {};
+      items.resize(np * size_t(hkv));
+      sc.placed.resize(np * size_t(hkv));
+      {
+        int32_t k = 0;
+        for (int32_t h = 0; h < hkv; ++h)
+          for (uint64_t pk : sc.packed) {
+            const int32_t r = int32_t(pk & 0xfffff);
+            const int32_t x = xcd_of_run(h, r), c = sc.run_cls[size_t(h) * size_t(runs) + size_t(r)];
+            const int32_t f0 = sc.run_first[size_t(r)], f1 = sc.run_first[size_t(r) + 1];
+            for (int32_t i = f0; i < f1; ++i, ++k) {
+              const Piece& pc = sc.pieces[size_t(i)];
+              sc.placed[size_t(k)] = Placed{x, c, i > f0 ? 1 : 0, i > f0 ? pc.start : 0,
+                                            kItemNs + int64_t(pc.g1 - pc.g0) * sc.block_ns[size_t(pc.tile)], k};
+              items[size_t(k)] = make_item(h, size_t(i));
+            }
+            cnt[x][c] += f1 - f0;
+          }
+      }
+      // bucket offsets; first pieces keep their order, later ones are sorted per bucket
+      int32_t off[kXcds][kSeClasses + 1], nfirst[kXcds][kSeClasses] = {};
+      {
+        int32_t at = 0;
+        for (int x = 0; x < kXcds; ++x)
+          for (int c = 0; c < kSeClasses; ++c) {
+            off[x][c] = at;
+            at += cnt[x][c];
+          }
+      }
+      {
+        int32_t fill[kXcds][kSeClasses];
+        for (int x = 0; x < kXcds; ++x)
+          for (int c = 0; c < kSeClasses; ++c) fill[x][c] = off[x][c];
+        for (const Placed& pl : sc.placed) nfirst[pl.xcd][pl.cls] += pl.later == 0;
+        // first pieces in dealing order, then later pieces
+        int32_t lat[kXcds][kSeClasses];
+        for (int x = 0; x < kXcds; ++x)
+          for (int c = 0; c < kSeClasses; ++c) lat[x][c] = off[x][c] + nfirst[x][c];
+        sc.by_xcd.resize(sc.placed.size());
+        for (uint32_t k = 0; k < sc.placed.size(); ++k) {
+          const Placed& pl = sc.placed[k];
+          sc.by_xcd[size_t(pl.later ? lat[pl.xcd][pl.cls]++ : fill[pl.xcd][pl.cls]++)] = k;
+        }
+        for (int x = 0; x < kXcds; ++x)
+          for (int c = 0; c < kSeClasses; ++c) {
+            auto b = sc.by_xcd.begin() + off[x][c] + nfirst[x][c], e = sc.by_xcd.begin() + off[x][c] + cnt[x][c];
+            std::sort(b, e, [&](uint32_t u, uint32_t v) {
+              const Placed &a = sc.placed[u], &q = sc.placed[v];
+              return a.key != q.key ? a.key < q.key : a.dur != q.dur ? a.dur > q.dur : u < v;
+            });
+          }
+      }
+      // workgroup (kSeClasses r + c) * kXcds + x: XCD x's (kSeClasses r + c)-th,
+      // on engine class c -- the r-th item of that class; a class with fewer
+      // items than the XCD's longest is padded with empty ones
+      size_t n_pos = 0;
+      for (int x = 0; x < kXcds; ++x) {
+        int32_t depth = 0;
+        for (int c = 0; c < kSeClasses; ++c) depth = std::max(depth, cnt[x][c]);
+        n_pos = std::max(n_pos, size_t(depth) * kSeClasses * kXcds);
+      }
+      WorkItem pad;
+      std::memset(&pad, 0, sizeof(pad));   // q_count 0: skipped by the kernels
+      pad.part_row = -1;
+      ordered_out.assign(n_pos, pad);
+      for (int x = 0; x < kXcds; ++x)
+        for (int c = 0; c < kSeClasses; ++c)
+          for (int32_t r = 0; r < cnt[x][c]; ++r)
+            ordered_out[(size_t(r) * kSeClasses + size_t(c)) * kXcds + size_t(x)] =
+                items[size_t(sc.placed[sc.by_xcd[size_t(off[x][c] + r)]].seq)];
+      while (!ordered_out.empty() && ordered_out.back().q_count == 0) ordered_out.pop_back();
     }
   }
 
@@ -342,14 +610,16 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   // so the tiles that stream one KV head stay together in one L2. Within an XCD
   // the longest items go first; an item's time grows with its key range times
   // its live 32-row waves. A size query (no meta_host) needs no order.
-  std::vector<int64_t>& cost = sc.cost;
-  cost.resize(items.size());
-  for (size_t i = 0; i < items.size(); ++i) {
-    const WorkItem& a = items[i];
-    cost[i] = int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
+  if (!streamed) {
+    std::vector<int64_t>& cost = sc.cost;
+    cost.resize(items.size());
+    for (size_t i = 0; i < items.size(); ++i) {
+      const WorkItem& a = items[i];
+      cost[i] = int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
+    }
+    if (meta_host) xcd_order(sc, n_groups);
   }
-  if (meta_host) xcd_order(sc, n_groups);
-  const std::vector<WorkItem>& ordered = meta_host ? sc.ordered : items;
+  const std::vector<WorkItem>& ordered = streamed || meta_host ? sc.ordered : items;
   const int32_t n_items = int32_t(ordered.size());
   const MetaLayout lay = meta_layout(batch, n_items, n_split_rows);
   if (meta_bytes_out) *meta_bytes_out = lay.total;
@@ -361,7 +631,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     max_blocks = std::max(max_blocks, nb);
     sum_blocks += nb;
   }
-  const int64_t slot_blocks = std::max(max_blocks, (sum_blocks + slots - 1) / slots);
+  const int64_t slot_blocks = streamed ? stream_blocks : std::max(max_blocks, (sum_blocks + slots - 1) / slots);
 
   if (plan) {
     std::memset(plan, 0, sizeof(*plan));
@@ -396,7 +666,18 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       pre[b] = prefix_lens[b];
     }
     if (n_items) std::memcpy(base + lay.items, ordered.data(), sizeof(WorkItem) * ordered.size());
-    if (n_split_rows) std::memcpy(base + lay.split_rows, split_rows.data(), sizeof(int32_t) * split_rows.size());
+    // split rows: (global token, split count) for every token of a split tile, in partial-row order
+    int32_t* sr = reinterpret_cast<int32_t*>(base + lay.split_rows);
+    for (size_t ti = 0; ti < tiles.size(); ++ti) {
+      if (tile_part[ti] < 0) continue;
+      const Tile& t = tiles[ti];
+      int32_t* row = sr + 2 * size_t(tile_part[ti]);
+      const int32_t tok = qo_start[size_t(t.req)] + t.q_begin;
+      for (int32_t i = 0; i < t.q_count; ++i) {
+        row[2 * i] = tok + i;
+        row[2 * i + 1] = tile_splits[ti];
+      }
+    }
   }
   return PKV_OK;
 }

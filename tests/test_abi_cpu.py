@@ -400,17 +400,62 @@ def test_plan_sized_for_the_given_compute_units():
     assert small.plan.n_items == 32 and small.plan.n_split_rows == 0 and small.plan.workspace_bytes == 0
     big = pkv.build_extend_metadata([3584], [512], s16, num_cus=256)
     assert big.plan.num_cus == 256 and 32 < big.plan.n_items <= 256 and big.plan.n_split_rows == 512
+    # 80 units: 32 tiles cut 2 or 3 ways leave the units uneven; the stream plan
+    # (runs of equal predicted time, some of two pieces) takes over
     mid = pkv.build_extend_metadata([3584], [512], s16, num_cus=80)
-    assert 32 < mid.plan.n_items <= 80
+    real = mid.host_sections()["items"]
+    assert 32 < len(real) <= 2 * 80 and mid.plan.n_items >= len(real)
+    coverage(mid, np.array([3584], np.int32), np.array([512], np.int32), 16, 4, 0)
     P, L = np.full(4, 20000, np.int32), np.ones(4, np.int32)
     for cus, want in ((32, 2), (64, 4), (256, 16), (1024, 32)):
         p = pkv.build_extend_metadata(P, L, shape(32, 8, 128, 16, 8000), num_cus=cus)
         assert p.plan.max_splits == want, (cus, p.plan.max_splits)
     # the size query plans the same list
-    for cus in (32, 256):
+    for cus in (32, 80, 256):
         mb, wb = pkv.extend_metadata_size([3584], [512], s16, num_cus=cus)
         p = pkv.build_extend_metadata([3584], [512], s16, num_cus=cus)
         assert mb == p.meta_host.size and wb == p.plan.workspace_bytes
+
+
+@pytest.mark.parametrize("P,L,cus", [(6144, 2048, 256), (2048, 2048, 256), (0, 512, 256), (1024, 128, 256),
+                                     (3584, 512, 80), (100, 300, 256)])
+def test_stream_plan_structure(P, L, cus):
+    """Plans whose equal cuts would leave the compute units uneven (a causal
+    chunk's later tiles see more keys) cut each KV head's work end to end into
+    runs of nearly equal predicted time. Every row stays covered once, each
+    tile keeps one split count for all KV heads (the combine reads one per
+    token), padding items are empty and come only after the last real item of
+    their XCD and shader-engine class, and the predicted load per XCD is even."""
+    s = shape(16, 4, 128, 64, 1000)
+    p = pkv.build_extend_metadata([P], [L], s, num_cus=cus)
+    h = p.host_sections()
+    coverage(p, np.array([P], np.int32), np.array([L], np.int32), 16, 4, 0)
+    items, pad = h["items"], h["padding"]
+    counts = {}
+    for it in items:
+        counts.setdefault(int(it["q_begin"]), set()).add((int(it["head_split"]) >> 8) & 0xFF)
+    assert all(len(v) == 1 for v in counts.values())
+    assert (pad["q_count"] == 0).all() and (pad["kv_begin"] == pad["kv_end"]).all() and (pad["part_row"] == -1).all()
+    # workgroup q runs on XCD q % 8, shader-engine class (q // 8) % 4 (in order per XCD):
+    # padding sits only after the last real item of its (XCD, class)
+    real_pos = set(int(x) for x in items["position"])
+    group = lambda q: (q % 8, (q // 8) % 4)  # noqa: E731
+    last_real = {}
+    for q in real_pos:
+        last_real[group(q)] = max(last_real.get(group(q), -1), q)
+    for q in range(p.plan.n_items):
+        if q not in real_pos:
+            assert q > last_real.get(group(q), -1), "padding before a real item of its engine class"
+    # predicted time per XCD (2.8 us per item, 1.39 + 0.067 w us per 64-key block) within 10 % of the mean
+    load = np.zeros(8)
+    for it in items:
+        blocks = -(-int(it["kv_end"]) // 64) - int(it["kv_begin"]) // 64
+        waves = min(8, -(-int(it["q_count"]) * 4 // 32))
+        load[int(it["position"]) % 8] += 2.8 + blocks * (1.39 + 0.067 * waves)
+    used = load[load > 0]
+    assert used.max() <= 1.1 * used.mean() + 3.0, load
+    mb, wb = pkv.extend_metadata_size([P], [L], s, num_cus=cus)
+    assert mb == p.meta_host.size and wb == p.plan.workspace_bytes
 
 
 def test_plan_without_device_uses_nominal_cus():
