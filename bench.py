@@ -398,6 +398,8 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
         "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope),
                    "explicit_mask": args.mask, "append": "fused" if fuse_mode else "separate",
+                   "split_partials": ("bf16 unnormalised output, fp32 (max, sum)" if w.dtype == "bf16"
+                                      else "fp32 unnormalised output, fp32 (max, sum)"),
                    "batches_per_step": len(B),
                    "query_tokens_per_step": tokens, "flops_per_step": flops},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
