@@ -105,7 +105,7 @@ struct Scratch {
   std::vector<uint32_t> by_xcd;
   // stream plan
   std::vector<int64_t> block_ns, run_load;
-  std::vector<int32_t> piece_count, piece_next;
+  std::vector<int32_t> piece_count, piece_next, bucket;
   std::vector<Piece> pieces;
   std::vector<Placed> placed;
   std::vector<int32_t> run_first, run_cls;
@@ -127,12 +127,30 @@ void xcd_order(Scratch& sc, int32_t ng) {
   std::vector<WorkItem>& out = sc.ordered;
   const size_t n = in.size();
   out.clear();
-  // Longest first, ties in the planner's order: one integer sort of
-  // (max cost - cost, index) packed into 64 bits (costs < 2^31 per item).
-  const int64_t cmax = n ? *std::max_element(c.begin(), c.end()) : 0;
+  // Longest first, ties in the planner's order: (max cost - cost, index)
+  // packed into 64 bits (costs < 2^31 per item), ordered by a counting sort
+  // when the costs span few values (the usual case: a launch's items come
+  // from a few tile shapes), else by a comparison sort.
+  int64_t cmax = 0, cmin = INT64_MAX;
+  for (size_t i = 0; i < n; ++i) {
+    cmax = std::max(cmax, c[i]);
+    cmin = std::min(cmin, c[i]);
+  }
   sc.packed.resize(n);
-  for (size_t i = 0; i < n; ++i) sc.packed[i] = (uint64_t(cmax - c[i]) << 32) | uint64_t(i);
-  std::sort(sc.packed.begin(), sc.packed.end());
+  constexpr int64_t kCountingRange = 4096;
+  if (n > 0 && cmax - cmin < kCountingRange) {
+    const size_t range = size_t(cmax - cmin) + 1;
+    sc.bucket.assign(range + 1, 0);
+    for (size_t i = 0; i < n; ++i) ++sc.bucket[size_t(cmax - c[i]) + 1];
+    for (size_t b = 0; b < range; ++b) sc.bucket[b + 1] += sc.bucket[b];
+    for (size_t i = 0; i < n; ++i) {
+      const uint64_t key = uint64_t(cmax - c[i]);
+      sc.packed[size_t(sc.bucket[size_t(key)]++)] = (key << 32) | uint64_t(i);
+    }
+  } else {
+    for (size_t i = 0; i < n; ++i) sc.packed[i] = (uint64_t(cmax - c[i]) << 32) | uint64_t(i);
+    std::sort(sc.packed.begin(), sc.packed.end());
+  }
   if (n < size_t(kXcds) * 2) {
     for (uint64_t pk : sc.packed) out.push_back(in[pk & 0xffffffffu]);
     return;
@@ -438,6 +456,13 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       cur_split += a.part_row >= 0;
     }
     const int64_t cur_cost = cur_max + kPartialNs * cur_split;
+    int64_t cur_sum = 0;
+    for (const WorkItem& a : items) {
+      const int64_t nb = a.kv_end > a.kv_begin ? ceil_div(a.kv_end, kSplitGranule) - a.kv_begin / kSplitGranule : 0;
+      cur_sum += kItemNs + nb * (kBlockNs + kBlockWaveNs * std::min<int64_t>(8, (int64_t(a.q_count) * group + 31) / 32));
+    }
+    // the equal cuts already load every slot within 1/16 of the mean: no cut does better by 1/32
+    const bool even = cur_max * 16 <= (cur_sum + slots - 1) / slots * 17;
     // Run time bounds: at least a piece of one block, and at least the block
     // work over the runs plus a prologue (every run has one); a greedy cut at
     // the work over the runs plus one prologue per tile over the runs, two more
@@ -458,7 +483,7 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     lo = std::min(lo, hi);
     // no cut can beat the plan above by 1/32 when even the bound cannot (a
     // near-even plan): skip the search
-    if (lo + lo / 32 >= cur_cost) hi = lo = -1;
+    if (even || lo + lo / 32 >= cur_cost) hi = lo = -1;
     else if (stream_cut(tiles, sc, hi, limit, false) > limit) hi = total;   // only the split cap can get here
     // the shortest run time (to within 1/256) whose cut fits
     while (hi > 0 && hi - lo > std::max<int64_t>(64, hi / 256)) {
@@ -615,7 +640,9 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     cost.resize(items.size());
     for (size_t i = 0; i < items.size(); ++i) {
       const WorkItem& a = items[i];
-      cost[i] = int64_t(a.kv_end - a.kv_begin) * ((int64_t(a.q_count) * group + 31) / 32);
+      const int64_t blocks =
+          a.kv_end > a.kv_begin ? ceil_div(a.kv_end, kSplitGranule) - a.kv_begin / kSplitGranule : 0;
+      cost[i] = blocks * ((int64_t(a.q_count) * group + 31) / 32);
     }
     if (meta_host) xcd_order(sc, n_groups);
   }
