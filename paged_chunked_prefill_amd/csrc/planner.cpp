@@ -447,20 +447,17 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
   std::vector<WorkItem>& ordered_out = sc.ordered;
   if (shape->dtype == PKV_DTYPE_BF16 && decode_splits == 0 && n_one < int32_t(tiles.size()) && runs_per_head >= 1 &&
       int64_t(items.size()) <= slots) {
-    // the plan above: its longest item (one per slot) and its partials
-    int64_t cur_max = 0, cur_split = 0;
+    // the plan above: its longest item (one per slot), its mean load per slot and its partials
+    int64_t cur_max = 0, cur_sum = 0, cur_split = 0;
     for (const WorkItem& a : items) {
       const int64_t nb = a.kv_end > a.kv_begin ? ceil_div(a.kv_end, kSplitGranule) - a.kv_begin / kSplitGranule : 0;
       const int64_t w = std::min<int64_t>(8, (int64_t(a.q_count) * group + 31) / 32);
-      cur_max = std::max(cur_max, kItemNs + nb * (kBlockNs + kBlockWaveNs * w));
+      const int64_t t = kItemNs + nb * (kBlockNs + kBlockWaveNs * w);
+      cur_max = std::max(cur_max, t);
+      cur_sum += t;
       cur_split += a.part_row >= 0;
     }
     const int64_t cur_cost = cur_max + kPartialNs * cur_split;
-    int64_t cur_sum = 0;
-    for (const WorkItem& a : items) {
-      const int64_t nb = a.kv_end > a.kv_begin ? ceil_div(a.kv_end, kSplitGranule) - a.kv_begin / kSplitGranule : 0;
-      cur_sum += kItemNs + nb * (kBlockNs + kBlockWaveNs * std::min<int64_t>(8, (int64_t(a.q_count) * group + 31) / 32));
-    }
     // the equal cuts already load every slot within 1/16 of the mean: no cut does better by 1/32
     const bool even = cur_max * 16 <= (cur_sum + slots - 1) / slots * 17;
     // Run time bounds: at least a piece of one block, and at least the block
@@ -481,27 +478,33 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
     int64_t lo = std::max(piece_min, (work + limit - 1) / limit + kItemNs);
     int64_t hi = std::min(total, (total + limit - 1) / limit + 2 * kItemNs + block_max);
     lo = std::min(lo, hi);
-    // no cut can beat the plan above by 1/32 when even the bound cannot (a
-    // near-even plan): skip the search
-    if (even || lo + lo / 32 >= cur_cost) hi = lo = -1;
-    else if (stream_cut(tiles, sc, hi, limit, false) > limit) hi = total;   // only the split cap can get here
-    // the shortest run time (to within 1/256) whose cut fits
-    while (hi > 0 && hi - lo > std::max<int64_t>(64, hi / 256)) {
-      const int64_t mid = lo + (hi - lo) / 2;
-      if (stream_cut(tiles, sc, mid, limit, false) <= limit) hi = mid; else lo = mid + 1;
+    // No cut can beat the plan above by 1/32 when even the bound cannot (a
+    // near-even plan): no search. Otherwise the shortest run time (to within
+    // 1/256) whose cut fits; at `total` everything fits one run, one piece a
+    // tile, so only the split cap can make `hi` fail.
+    int32_t runs = 0;
+    if (!even && lo + lo / 32 < cur_cost) {
+      if (stream_cut(tiles, sc, hi, limit, false) > limit) hi = total;
+      while (hi - lo > std::max<int64_t>(64, hi / 256)) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (stream_cut(tiles, sc, mid, limit, false) <= limit) hi = mid; else lo = mid + 1;
+      }
+      runs = stream_cut(tiles, sc, hi, limit, true);
     }
-    const int32_t runs = hi > 0 ? stream_cut(tiles, sc, hi, limit, true) : 0;
-    sc.run_load.assign(size_t(runs), 0);
+    // the cut's predicted time: its busiest run plus the partials of split tiles
+    int64_t stream_cost = 0;
     std::vector<int64_t>& run_blocks = sc.cost;   // (free until the dispatch order below)
-    run_blocks.assign(size_t(runs), 0);
-    for (const Piece& pc : sc.pieces) {
-      sc.run_load[size_t(pc.run)] += kItemNs + int64_t(pc.g1 - pc.g0) * sc.block_ns[size_t(pc.tile)];
-      run_blocks[size_t(pc.run)] += pc.g1 - pc.g0;
+    if (runs > 0) {
+      sc.run_load.assign(size_t(runs), 0);
+      run_blocks.assign(size_t(runs), 0);
+      for (const Piece& pc : sc.pieces) {
+        sc.run_load[size_t(pc.run)] += kItemNs + int64_t(pc.g1 - pc.g0) * sc.block_ns[size_t(pc.tile)];
+        run_blocks[size_t(pc.run)] += pc.g1 - pc.g0;
+      }
+      int64_t split_pieces = 0;
+      for (int32_t c : sc.piece_count) split_pieces += c > 1 ? c : 0;
+      stream_cost = *std::max_element(sc.run_load.begin(), sc.run_load.end()) + kPartialNs * hkv * split_pieces;
     }
-    int64_t split_pieces = 0;
-    for (int32_t c : sc.piece_count) split_pieces += c > 1 ? c : 0;
-    const int64_t stream_cost =
-        runs > 0 ? *std::max_element(sc.run_load.begin(), sc.run_load.end()) + kPartialNs * hkv * split_pieces : 0;
     if (runs > 0 && stream_cost + stream_cost / 32 < cur_cost) {
       streamed = true;
       stream_blocks = *std::max_element(run_blocks.begin(), run_blocks.end());
