@@ -150,6 +150,9 @@ def main():
                     help="fused (default): paged_extend_attn_append, whose bf16 attention launch also writes the "
                          "chunk's K/V into the pool when the plan's slot_blocks <= 128 (else it runs the append "
                          "kernel first); separate: pkv_append then paged_extend_attn")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="attention layers per batch: the batch's plan is built (and copied) once and every "
+                         "layer runs its own append + attention on its own K/V pools, queries and outputs")
     ap.add_argument("--rope", action="store_true",
                     help="the step rotates q and k at their absolute positions with pkv_rope_append (in place "
                          "of pkv_append) before the attention; reports that kernel's HBM rate")
@@ -201,6 +204,10 @@ def main():
     if prefill_prefix:
         cache.fill_prefix(w)
     nsteps = args.warmup + args.steps
+    if args.layers < 1:
+        raise SystemExit("--layers must be >= 1")
+    # pools of layers 1.. (--layers): copies of the cache's pools as they stand after the prefix was written
+    layer_pools = [(cache.k_pool.clone(), cache.v_pool.clone()) for _ in range(1, args.layers)]
 
     # rotary table (cos, sin) of every position the workload reaches, for --rope
     import workloads as wl
@@ -231,47 +238,63 @@ def main():
         b["meta_args"] = [(len(L), P.ctypes.data_as(ctypes.c_void_p), L.ctypes.data_as(ctypes.c_void_p),
                            ctypes.byref(shape), bw.window, splits, vp(h), meta_bytes, vp(meta_dev), meta_bytes,
                            ctypes.byref(plan), sh) for h in hosts]
-        if args.rope:
-            # q is rotated into q_rot, which the attention reads; per token the kernel moves q, K and V
-            # in and out once and reads one table row
-            b["q_rot"] = torch.empty_like(q)
-            b["append_fn"] = lib.pkv_rope_append
-            b["append_args"] = (vp(q), vp(b["q_rot"]), vp(kn), vp(vn), vp(rope_table), rope_table.shape[0],
-                                vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table), cache.page_table.shape[1],
-                                None, ctypes.byref(plan), ctypes.byref(shape), sh)
-            b["append_bytes"] = int(L.sum()) * (2 * esize * w.head_dim * (w.num_q_heads + 2 * w.num_kv_heads) +
-                                                4 * w.head_dim)
-        else:
-            b["append_fn"] = lib.pkv_append
-            b["append_args"] = (vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
-                                cache.page_table.shape[1], None, ctypes.byref(plan), ctypes.byref(shape), sh)
-            b["append_bytes"] = int(L.sum()) * 4 * esize * w.head_dim * w.num_kv_heads
-        q_attn = b["q_rot"] if args.rope else q
-        if args.mask == "none":
-            b["attn_fn"] = lib.paged_extend_attn
-            b["attn_args"] = (vp(q_attn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
-                              cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, ctypes.byref(plan),
-                              ctypes.byref(shape), vp(out), vp(ws), ws.numel(), sh)
-        else:
+        def calls_for(q, out, k_pool, v_pool):
+            """(append fn, its args, attention fn, its args, rotated-q buffer) of one layer's batch call."""
+            append_fn = append_args = q_rot = None
+            if args.rope:
+                # q is rotated into q_rot, which the attention reads; per token the kernel moves q, K and V
+                # in and out once and reads one table row
+                q_rot = torch.empty_like(q)
+                append_fn = lib.pkv_rope_append
+                append_args = (vp(q), vp(q_rot), vp(kn), vp(vn), vp(rope_table), rope_table.shape[0],
+                               vp(k_pool), vp(v_pool), vp(cache.page_table), cache.page_table.shape[1],
+                               None, ctypes.byref(plan), ctypes.byref(shape), sh)
+            else:
+                append_fn = lib.pkv_append
+                append_args = (vp(kn), vp(vn), vp(k_pool), vp(v_pool), vp(cache.page_table),
+                               cache.page_table.shape[1], None, ctypes.byref(plan), ctypes.byref(shape), sh)
+            q_attn = q_rot if args.rope else q
+            if args.mask == "none":
+                attn_fn = lib.paged_extend_attn
+                attn_args = (vp(q_attn), vp(k_pool), vp(v_pool), vp(cache.page_table),
+                             cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, ctypes.byref(plan),
+                             ctypes.byref(shape), vp(out), vp(ws), ws.numel(), sh)
+            else:
+                attn_fn = lib.paged_extend_attn_masked
+                attn_args = (vp(q_attn), vp(k_pool), vp(v_pool), vp(cache.page_table),
+                             cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, vp(b["mask"]), mh,
+                             int(L.max()), ks, ctypes.byref(plan), ctypes.byref(shape), vp(out), vp(ws), ws.numel(),
+                             sh)
+            if fuse_mode:
+                append_fn = append_args = None
+                attn_fn = lib.paged_extend_attn_append
+                attn_args = (vp(q), vp(kn), vp(vn), vp(k_pool), vp(v_pool), vp(cache.page_table),
+                             cache.page_table.shape[1], None, bw.window, 0.0, ctypes.byref(plan),
+                             ctypes.byref(shape), vp(out), vp(ws), ws.numel(), sh)
+            return append_fn, append_args, attn_fn, attn_args, q_rot
+
+        if args.mask != "none":
             ks = (int((P + L).max()) + 3) // 4 * 4
             mh = w.num_q_heads if args.mask == "heads" else 1
             b["mask"] = torch.ones((len(L), mh, int(L.max()), ks), dtype=torch.uint8, device=dev)
-            b["attn_fn"] = lib.paged_extend_attn_masked
-            b["attn_args"] = (vp(q_attn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
-                              cache.page_table.shape[1], None, None, None, None, bw.window, 0.0, vp(b["mask"]), mh,
-                              int(L.max()), ks, ctypes.byref(plan), ctypes.byref(shape), vp(out), vp(ws), ws.numel(),
-                              sh)
-        if fuse_mode:
-            b["append_fn"] = None
-            b["attn_fn"] = lib.paged_extend_attn_append
-            b["attn_args"] = (vp(q), vp(kn), vp(vn), vp(cache.k_pool), vp(cache.v_pool), vp(cache.page_table),
-                              cache.page_table.shape[1], None, bw.window, 0.0, ctypes.byref(plan),
-                              ctypes.byref(shape), vp(out), vp(ws), ws.numel(), sh)
+        # layer 0 uses the cache's pools, q and out; each further layer (--layers) its own copies of
+        # them (the pools as they stand after the prefix was written), all under the batch's one plan
+        b["layers"] = [calls_for(q, out, cache.k_pool, cache.v_pool)]
+        b["keep"] = []   # layer tensors, alive as long as their pointers are in use
+        for li in range(1, args.layers):
+            kp_l, vp_l = layer_pools[li - 1]
+            q_l, out_l = q.clone(), torch.empty_like(out)
+            b["keep"] += [q_l, out_l]
+            b["layers"].append(calls_for(q_l, out_l, kp_l, vp_l))
+        b["keep_rot"] = [c[4] for c in b["layers"]]
+        tq = int(L.sum())
+        b["append_bytes"] = (tq * (2 * esize * w.head_dim * (w.num_q_heads + 2 * w.num_kv_heads) + 4 * w.head_dim)
+                             if args.rope else tq * 4 * esize * w.head_dim * w.num_kv_heads)
         B.append(b)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    hev = HipEvents(2 * nsteps * len(B))   # (step s, batch i): events 2(s*len(B)+i) and +1
+    hev = HipEvents(2 * nsteps * len(B) * args.layers)   # (step s, batch i, layer l): 2((s*len(B)+i)*layers+l), +1
     evs, rec = hev.ev, hev.record
     build = lib.build_extend_metadata
 
@@ -279,15 +302,16 @@ def main():
         for i, b in enumerate(B):
             if build(*b["meta_args"][s]):
                 raise RuntimeError(lib.pkv_last_error().decode())
-            if b["append_fn"] is not None and b["append_fn"](*b["append_args"]):
-                raise RuntimeError(lib.pkv_last_error().decode())
-            k = 2 * (s * len(B) + i)
-            if bracket:
-                rec(evs[k], sh)
-            if b["attn_fn"](*b["attn_args"]):
-                raise RuntimeError(lib.pkv_last_error().decode())
-            if bracket:
-                rec(evs[k + 1], sh)
+            for li, (append_fn, append_args, attn_fn, attn_args, _) in enumerate(b["layers"]):
+                if append_fn is not None and append_fn(*append_args):
+                    raise RuntimeError(lib.pkv_last_error().decode())
+                k = 2 * ((s * len(B) + i) * args.layers + li)
+                if bracket:
+                    rec(evs[k], sh)
+                if attn_fn(*attn_args):
+                    raise RuntimeError(lib.pkv_last_error().decode())
+                if bracket:
+                    rec(evs[k + 1], sh)
 
     for s in range(args.warmup):
         step(s, False)
@@ -308,8 +332,10 @@ def main():
         step(s, True)
     torch.cuda.synchronize()
 
-    attn_ms = [sum(hev.elapsed_ms(2 * (s * len(B) + i), 2 * (s * len(B) + i) + 1)
-                   for s in range(args.warmup, nsteps)) / args.steps for i in range(len(B))]
+    # per batch: its attention calls over every layer
+    attn_ms = [sum(hev.elapsed_ms(2 * ((s * len(B) + i) * args.layers + li), 2 * ((s * len(B) + i) * args.layers + li) + 1)
+                   for s in range(args.warmup, nsteps) for li in range(args.layers)) / args.steps
+               for i in range(len(B))]
     hev.close()
     # the appends (or rotary appends) of a step, timed in a pass of their own after the timed steps so that
     # their events do not add to the step (rewriting the same slots and q rows: idempotent)
@@ -317,23 +343,24 @@ def main():
     e0.record(stream)
     for _ in range(args.steps):
         for b in B:
-            if b["append_fn"] is not None and b["append_fn"](*b["append_args"]):
-                raise RuntimeError(lib.pkv_last_error().decode())
+            for append_fn, append_args, _, _, _ in b["layers"]:
+                if append_fn is not None and append_fn(*append_args):
+                    raise RuntimeError(lib.pkv_last_error().decode())
     e1.record(stream)
     torch.cuda.synchronize()
     append_ms = e0.elapsed_time(e1) / args.steps
-    append_bytes = sum(b["append_bytes"] for b in B)
-    flops = sum(b["flops"] for b in B)
-    hbm_bytes = sum(b["bytes"] for b in B)
+    append_bytes = sum(b["append_bytes"] for b in B) * args.layers
+    flops = sum(b["flops"] for b in B) * args.layers
+    hbm_bytes = sum(b["bytes"] for b in B) * args.layers
     tokens = sum(b["total_q"] for b in B)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     attn_total_ms = sum(attn_ms)
     attn_tflops = flops / (attn_total_ms * 1e-3) / 1e12
     attn_gbs = hbm_bytes / (attn_total_ms * 1e-3) / 1e9
-    n_launch = len(B)
+    n_launch = len(B) * args.layers
     # launches whose append ran inside the attention kernel (paged_extend_attn_append's choice)
-    n_fused = sum(1 for b in B if fuse_mode and w.dtype == "bf16" and b["plan"].total_q > 0 and
-                  b["plan"].slot_blocks <= FUSE_MAX_SLOT_BLOCKS)
+    n_fused = args.layers * sum(1 for b in B if fuse_mode and w.dtype == "bf16" and b["plan"].total_q > 0 and
+                                b["plan"].slot_blocks <= FUSE_MAX_SLOT_BLOCKS)
     decode_bound = args.workload == "decode64"
     roofline = {
         "kernel": f"extend_attn_{w.dtype}<{w.head_dim}>" + (
@@ -398,6 +425,7 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, shuffled page tables)",
         "config": {"workload": desc, "name": args.workload, "rotary_append": bool(args.rope),
                    "explicit_mask": args.mask, "append": "fused" if fuse_mode else "separate",
+                   "layers": args.layers,
                    "split_partials": ("bf16 unnormalised output, fp32 (max, sum)" if w.dtype == "bf16"
                                       else "fp32 unnormalised output, fp32 (max, sum)"),
                    "batches_per_step": len(B),
@@ -407,7 +435,7 @@ def main():
         "mfma_peak_frac": round(tflops / MFMA_PEAK_BF16, 4),
         "attn_only": {"ms_per_step": round(attn_total_ms, 4), "tflops": round(attn_tflops, 3),
                       "mfma_peak_frac": round(attn_tflops / MFMA_PEAK_BF16, 4),
-                      "hbm_gbs_algorithmic": round(attn_gbs, 1), "per_launch_ms": [round(x, 4) for x in attn_ms]},
+                      "hbm_gbs_algorithmic": round(attn_gbs, 1), "per_launch_ms": [round(x / args.layers, 4) for x in attn_ms]},
         "roofline": roofline, "cpu_baseline": cpu, "setup_s": round(setup_s, 2),
     }
     rope_cpu = None
@@ -440,9 +468,9 @@ def time_graph_replay(args, B, lib, flops, tokens):
     for b in B:
         if lib.build_extend_metadata(*b["meta_args"][0]):
             raise RuntimeError(lib.pkv_last_error().decode())
-        ap = b["append_args"][:-1] + (sh,)
-        at = b["attn_args"][:-1] + (sh,)
-        calls.append((b["append_fn"], ap, b["attn_fn"], at))
+        for append_fn, append_args, attn_fn, attn_args, _ in b["layers"]:
+            ap = append_args[:-1] + (sh,) if append_args is not None else None
+            calls.append((append_fn, ap, attn_fn, attn_args[:-1] + (sh,)))
     torch.cuda.synchronize()
 
     def step():
