@@ -111,7 +111,9 @@ struct Scratch {
   std::vector<int32_t> piece_count, piece_next, bucket;
   std::vector<Piece> pieces;
   std::vector<Placed> placed;
-  std::vector<int32_t> run_first, run_cls;
+  std::vector<int32_t> run_first, run_cls, run_xcd;
+  std::vector<WorkItem> piece_item;
+  std::vector<int64_t> piece_dur;
 };
 
 Scratch& scratch() {
@@ -563,7 +565,13 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
       // (head, run) -> XCD; per XCD the runs in that order are dealt to the
       // engine classes in turn (rank mod kSeClasses), heads one after another
       const int64_t total_runs = int64_t(runs) * hkv;   // <= slots: at most slots / 8 runs per XCD
-      auto xcd_of_run = [&](int32_t h, int32_t r) { return int32_t((int64_t(h) * runs + r) * kXcds / total_runs); };
+      // run j = h * runs + r goes to XCD floor(8 j / total_runs) (a table, no division per run)
+      sc.run_xcd.resize(size_t(total_runs));
+      for (int64_t j = 0, x = 0; j < total_runs; ++j) {
+        while ((x + 1) * total_runs <= j * kXcds) ++x;
+        sc.run_xcd[size_t(j)] = int32_t(x);
+      }
+      auto xcd_of_run = [&](int32_t h, int32_t r) { return sc.run_xcd[size_t(h) * size_t(runs) + size_t(r)]; };
       sc.run_cls.assign(size_t(total_runs), 0);
       int32_t rank[kXcds] = {};
       for (int32_t h = 0; h < hkv; ++h)
@@ -572,22 +580,25 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
           sc.run_cls[size_t(h) * size_t(runs) + size_t(r)] = rank[xcd_of_run(h, r)]++ % kSeClasses;
         }
       // items, then (XCD, class) buckets: the first pieces in the dealing
-      // order above, then the later pieces by predicted start
-      auto make_item = [&](int32_t h, size_t i) {
+      // order above, then the later pieces by predicted start. Each piece's
+      // item (KV head 0) and predicted duration, once for every head.
+      sc.piece_item.resize(np);
+      sc.piece_dur.resize(np);
+      for (size_t i = 0; i < np; ++i) {
         const Piece& pc = sc.pieces[i];
         const Tile& tl = tiles[size_t(pc.tile)];
         const int32_t S = sc.piece_count[size_t(pc.tile)];
-        WorkItem it;
+        WorkItem& it = sc.piece_item[i];
         it.req = tl.req;
-        it.head_split = (h << (2 * kSplitBits)) | (S << kSplitBits) | gid[i];
+        it.head_split = (S << kSplitBits) | gid[i];
         it.tok0 = qo_start[size_t(tl.req)] + tl.q_begin;
         it.pos0 = causal ? prefix_lens[tl.req] + tl.q_begin : kNonCausalPos;
         it.q_count = tl.q_count;
         it.kv_begin = std::max(tl.kv_lo, pc.g0 * kSplitGranule);
         it.kv_end = std::min(tl.kv_hi, pc.g1 * kSplitGranule);
         it.part_row = tile_part[size_t(pc.tile)];
-        return it;
-      };
+        sc.piece_dur[i] = kItemNs + int64_t(pc.g1 - pc.g0) * sc.block_ns[size_t(pc.tile)];
+      }
       int32_t cnt[kXcds][kSeClasses] = {};
       items.resize(np * size_t(hkv));
       sc.placed.resize(np * size_t(hkv));
@@ -599,10 +610,11 @@ int plan_extend(int32_t batch, const int32_t* prefix_lens, const int32_t* chunk_
             const int32_t x = xcd_of_run(h, r), c = sc.run_cls[size_t(h) * size_t(runs) + size_t(r)];
             const int32_t f0 = sc.run_first[size_t(r)], f1 = sc.run_first[size_t(r) + 1];
             for (int32_t i = f0; i < f1; ++i, ++k) {
-              const Piece& pc = sc.pieces[size_t(i)];
-              sc.placed[size_t(k)] = Placed{x, c, i > f0 ? 1 : 0, i > f0 ? pc.start : 0,
-                                            kItemNs + int64_t(pc.g1 - pc.g0) * sc.block_ns[size_t(pc.tile)], k};
-              items[size_t(k)] = make_item(h, size_t(i));
+              sc.placed[size_t(k)] =
+                  Placed{x, c, i > f0 ? 1 : 0, i > f0 ? sc.pieces[size_t(i)].start : 0, sc.piece_dur[size_t(i)], k};
+              WorkItem& it = items[size_t(k)];
+              it = sc.piece_item[size_t(i)];
+              it.head_split |= h << (2 * kSplitBits);
             }
             cnt[x][c] += f1 - f0;
           }
