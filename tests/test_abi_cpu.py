@@ -417,9 +417,10 @@ def test_plan_sized_for_the_given_compute_units():
         assert mb == p.meta_host.size and wb == p.plan.workspace_bytes
 
 
-@pytest.mark.parametrize("P,L,cus", [(6144, 2048, 256), (2048, 2048, 256), (0, 512, 256), (1024, 128, 256),
-                                     (3584, 512, 80), (100, 300, 256)])
-def test_stream_plan_structure(P, L, cus):
+@pytest.mark.parametrize("P,L,cus,window", [(6144, 2048, 256, 0), (2048, 2048, 256, 0), (0, 512, 256, 0),
+                                            (1024, 128, 256, 0), (3584, 512, 80, 0), (100, 300, 256, 0),
+                                            (0, 512, 256, 128), (500, 300, 256, 1000)])
+def test_stream_plan_structure(P, L, cus, window):
     """Plans whose equal cuts would leave the compute units uneven (a causal
     chunk's later tiles see more keys) cut each KV head's work end to end into
     runs of nearly equal predicted time. Every row stays covered once, each
@@ -427,9 +428,12 @@ def test_stream_plan_structure(P, L, cus):
     token), padding items are empty and come only after the last real item of
     their XCD and shader-engine class, and the predicted load per XCD is even."""
     s = shape(16, 4, 128, 64, 1000)
-    p = pkv.build_extend_metadata([P], [L], s, num_cus=cus)
+    p = pkv.build_extend_metadata([P], [L], s, window, num_cus=cus)
     h = p.host_sections()
-    coverage(p, np.array([P], np.int32), np.array([L], np.int32), 16, 4, 0)
+    coverage(p, np.array([P], np.int32), np.array([L], np.int32), 16, 4, window)
+    equal = pkv.build_extend_metadata([P], [L], s, window, 1, num_cus=cus).host_sections()["items"]
+    assert len(h["items"]) != len(equal) or len(h["padding"]) or not np.array_equal(h["items"], equal), \
+        "expected a stream plan"
     items, pad = h["items"], h["padding"]
     counts = {}
     for it in items:
@@ -454,7 +458,7 @@ def test_stream_plan_structure(P, L, cus):
         load[int(it["position"]) % 8] += 2.8 + blocks * (1.39 + 0.067 * waves)
     used = load[load > 0]
     assert used.max() <= 1.1 * used.mean() + 3.0, load
-    mb, wb = pkv.extend_metadata_size([P], [L], s, num_cus=cus)
+    mb, wb = pkv.extend_metadata_size([P], [L], s, window, num_cus=cus)
     assert mb == p.meta_host.size and wb == p.plan.workspace_bytes
 
 

@@ -96,27 +96,30 @@ def test_fused_matches_two_calls_and_oracle(dtype, P, L, hq, hkv, D, ps, window,
     check_oracle(f"{dtype} P={P} L={L} {hq}/{hkv} D={D} ps={ps} W={window} S={splits}", out, w)
 
 
-@pytest.mark.parametrize("P,L,hq,hkv,D,ps", [
-    ([0], [512], 16, 4, 128, 64),          # the 4097-token prompt's first 512-token chunk
-    ([1024], [512], 16, 4, 128, 64),       # padding items between real ones
-    ([2048], [128], 16, 4, 128, 64),       # 17 pieces per tile
-    ([0], [512], 8, 2, 64, 16),            # D = 64
-    ([3000], [1000], 32, 4, 128, 16),      # G = 8, runs of two pieces, padding
-    ([1500, 0], [300, 200], 16, 2, 64, 16),   # two requests in one stream
-    ([0], [1536], 32, 8, 128, 16),         # 8 KV heads (one XCD each), runs of several pieces
+@pytest.mark.parametrize("P,L,hq,hkv,D,ps,window", [
+    ([0], [512], 16, 4, 128, 64, 0),          # the 4097-token prompt's first 512-token chunk
+    ([1024], [512], 16, 4, 128, 64, 0),       # padding items between real ones
+    ([2048], [128], 16, 4, 128, 64, 0),       # 17 pieces per tile
+    ([0], [512], 8, 2, 64, 16, 0),            # D = 64
+    ([3000], [1000], 32, 4, 128, 16, 0),      # G = 8, runs of two pieces, padding
+    ([1500, 0], [300, 200], 16, 2, 64, 16, 0),   # two requests in one stream
+    ([0], [1536], 32, 8, 128, 16, 0),         # 8 KV heads (one XCD each), runs of several pieces
+    ([0], [512], 16, 4, 128, 16, 128),        # sliding window: pieces start inside the window, padding
+    ([500], [300], 16, 4, 128, 16, 1000),     # window reaching into the prefix, padding
+    ([0], [1024], 16, 2, 64, 16, 256),        # window at D = 64
 ])
-def test_stream_plans(P, L, hq, hkv, D, ps):
+def test_stream_plans(P, L, hq, hkv, D, ps, window):
     """Plans whose work list is cut end to end per KV head (stream plans, with
     runs of several pieces and padding items): fused and two-call paths agree
     bit for bit and match the oracle; the automatic plan is a stream plan, i.e.
     differs from the equal cuts that an explicit split count selects."""
-    w = small("bf16", P, L, hq, hkv, D, ps)
+    w = small("bf16", P, L, hq, hkv, D, ps, window)
     Pa, La, s = np.array(P, np.int32), np.array(L, np.int32), shape_of(w)
-    auto = pkv.build_extend_metadata(Pa, La, s, 0, 0, num_cus=256).host_sections()["items"]
-    equal = pkv.build_extend_metadata(Pa, La, s, 0, 1, num_cus=256).host_sections()["items"]
+    auto = pkv.build_extend_metadata(Pa, La, s, window, 0, num_cus=256).host_sections()["items"]
+    equal = pkv.build_extend_metadata(Pa, La, s, window, 1, num_cus=256).host_sections()["items"]
     assert len(auto) != len(equal) or not np.array_equal(auto, equal), "expected a stream plan"
     out, _, _ = fused_and_two_call(w)
-    check_oracle(f"stream plan P={P} L={L} {hq}/{hkv} D={D} ps={ps}", out, w)
+    check_oracle(f"stream plan P={P} L={L} {hq}/{hkv} D={D} ps={ps} W={window}", out, w)
 
 
 @pytest.mark.parametrize("P,L,hq,hkv,D", [([100, 37, 0], [64, 200, 1], 16, 4, 128), ([0], [300], 8, 8, 64)])
