@@ -787,35 +787,51 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   };
   {
     const uint32_t wrow = piece_base(l32 / T::RPI) + uint32_t(l32 % T::RPI) * T::ROWB;
+    // (a split's partial is stored unscaled: no multiply)
+    auto stage = [&](auto scaled) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < T::DBLK; ++db)
+      for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 v;
+        for (int jj = 0; jj < 4; ++jj) {
+          bf16x4 v;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = (__bf16)(o[db][4 * jj + x] * scale_out);
-        const int chunk = (4 * db + jj) ^ T::kswz(l32);
-        *reinterpret_cast<u32x2*>(smem + wrow + 16 * chunk + 8 * half) = __builtin_bit_cast(u32x2, v);
-      }
+          for (int x = 0; x < 4; ++x)
+            v[x] = (__bf16)(decltype(scaled)::value ? o[db][4 * jj + x] * scale_out : o[db][4 * jj + x]);
+          const int chunk = (4 * db + jj) ^ T::kswz(l32);
+          *reinterpret_cast<u32x2*>(smem + wrow + 16 * chunk + 8 * half) = __builtin_bit_cast(u32x2, v);
+        }
+    };
+    if (split_item)
+      stage(std::false_type{});
+    else
+      stage(std::true_type{});
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back by other lanes
+  // every piece read back first (their reads overlap), then stored
   const int ec = lane % T::CH;
+  u32x4 val[PIECES];
+#pragma unroll
+  for (int g = 0; g < PIECES; ++g)
+    val[g] = *reinterpret_cast<const u32x4*>(smem + piece_base(g) + (lane / T::CH) * T::ROWB +
+                                             16 * (ec ^ T::kswz(T::RPI * g + lane / T::CH)));
+  // row (token t, query head h) of the output, or of this split's partials:
+  // dst0 + (t Hq + h) * row_stride, with t Hq + h < 256 Hq < 2^30 and
+  // row_stride = D or max_splits D (< 2^13)
+  uint16_t* const dst0 =
+      split_item ? static_cast<uint16_t*>(p.o_part) + (int64_t(it.part_row) * p.num_q_heads * p.max_splits + it.split) * D
+                 : static_cast<uint16_t*>(p.out) + int64_t(it.tok0) * p.num_q_heads * D;
+  const uint32_t row_stride = uint32_t(split_item ? p.max_splits : 1) * D;
+  const int tok_end = min(it.q_count, p.total_q - it.tok0);
   // token = row / G for rows < 256 and G <= 128: (row * ceil(2^16 / G)) >> 16 is exact
   const uint32_t inv_g = (65536u + uint32_t(G) - 1) / uint32_t(G);
+  // tile row r = t G + j is query head kv_head G + j of token t: t Hq + h = t (Hq - G) + kv_head G + r
+  const int hq_minus_g = p.num_q_heads - G, head0 = it.kv_head * G;
 #pragma unroll
   for (int g = 0; g < PIECES; ++g) {
-    const int er = T::RPI * g + lane / T::CH;   // row within the wave's tile
-    const u32x4 val =
-        *reinterpret_cast<const u32x4*>(smem + piece_base(g) + (lane / T::CH) * T::ROWB + 16 * (ec ^ T::kswz(er)));
-    const int rr = wave * 32 + er;              // tile row = token * G + head-in-group
+    const int rr = wave * 32 + T::RPI * g + lane / T::CH;   // tile row = token * G + head-in-group
     const int etok = int((uint32_t(rr) * inv_g) >> 16);
-    const int ehead = it.kv_head * G + (rr - etok * G);
-    if (etok >= it.q_count || it.tok0 + etok >= p.total_q) continue;
-    uint16_t* dst = split_item
-        ? static_cast<uint16_t*>(p.o_part) +
-              ((int64_t(it.part_row + etok) * p.num_q_heads + ehead) * p.max_splits + it.split) * D
-        : static_cast<uint16_t*>(p.out) + (int64_t(it.tok0 + etok) * p.num_q_heads + ehead) * D;
-    *reinterpret_cast<u32x4*>(dst + 8 * ec) = val;
+    const uint32_t row = uint32_t(etok * hq_minus_g + head0 + rr);
+    if (etok < tok_end) *reinterpret_cast<u32x4*>(dst0 + uint64_t(row) * row_stride + 8 * ec) = val[g];
   }
 }
 
