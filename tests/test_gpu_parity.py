@@ -281,6 +281,21 @@ def test_variants(dtype, D, hq, hkv, ps, window):
     check(f"variant {dtype} D={D} {hq}/{hkv} ps={ps} W={window}", out, oracle_out(w, oracle_pools(w)), dtype)
 
 
+@pytest.mark.parametrize("D,hq,hkv,ps", [(128, 6, 2, 16), (64, 12, 4, 7), (128, 40, 8, 16)])
+def test_split_partials_odd_group(D, hq, hkv, ps):
+    """Split items whose GQA group does not divide the 4-row pieces of the
+    output store (G = 3 and 5): the partial rows (token x query head) of every
+    split land where the combine reads them."""
+    P = np.array([1500, 700, 0], np.int32)
+    L = np.array([40, 90, 33], np.int32)
+    pages = int(sum((int(n) + ps - 1) // ps for n in P + L)) + 5
+    w = wl.Workload("odd-group splits", 44, "bf16", hq, hkv, D, ps, pages, 0, P, L,
+                    wl.shuffled_page_table(44, pages, P + L, ps))
+    out, _, plan = prefill_and_attend(w)
+    assert plan.plan.n_split_rows > 0 and plan.plan.max_splits > 1, "expected split rows"
+    check(f"odd-group splits D={D} {hq}/{hkv} ps={ps}", out, oracle_out(w, oracle_pools(w)), "bf16")
+
+
 # Short chunks and one-token rows whose rows all fit one 16-row block
 # (max_q_len * G <= 16), with splits, windows and small pages.
 @pytest.mark.parametrize("hq,hkv,ps,P,L,window,splits", [
