@@ -190,6 +190,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "copy_calibration":
         return copy_calibration(args)
+    if args.workload == "gemm_calibration":
+        return gemm_calibration(args)
     if not pkv.device_supported(0):
         raise SystemExit("device 0 is not gfx950")
     lib = pkv.lib()
@@ -632,6 +634,33 @@ def copy_calibration(args):
     torch.cuda.synchronize()
     print(json.dumps({"workload": "copy_calibration", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                       "launches": args.warmup + args.steps}), flush=True)
+
+
+def gemm_calibration(args):
+    """What the device's own dense bf16 contraction sustains: torch.matmul
+    (hipBLASLt) on square bf16 matrices of 4096, 8192 and 16384, timed with
+    events over --steps launches after --warmup. A reference point for the
+    attention kernel's fraction of the 2.5 PFLOP/s peak, not a bench line."""
+    import torch
+    rows = []
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(max(args.warmup, 1)):
+            c = a @ b
+        steps = max(1, args.steps if n < 16384 else args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        rows.append({"n": n, "ms": round(ms, 4), "tflops": round(tf, 1), "peak_frac": round(tf / MFMA_PEAK_BF16, 4)})
+        del a, b, c
+    print(json.dumps({"workload": "gemm_calibration", "op": "torch.matmul bf16 (hipBLASLt), square n x n x n",
+                      "results": rows}), flush=True)
 
 
 def cpu_rope_baseline(batches, w, table_np):
