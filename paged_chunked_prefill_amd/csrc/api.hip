@@ -333,7 +333,8 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
                             int32_t window, float sm_scale, const uint8_t* mask, int32_t mask_heads,
                             int32_t mask_rows, int32_t mask_kv_stride, const pkv_plan* plan, const pkv_shape* shape,
                             void* out, void* workspace, size_t workspace_bytes, pkv_stream_t stream,
-                            const void* k_new = nullptr, const void* v_new = nullptr) {
+                            const void* k_new = nullptr, const void* v_new = nullptr,
+                            bool validate_only = false) {
   g_error[0] = 0;
   int st = check_plan(plan, shape, name);
   if (st) return st;
@@ -383,6 +384,7 @@ static int extend_attn_call(const char* name, const void* q, const void* k_pool,
                        workspace_bytes, plan->workspace_bytes);
   }
   if ((st = check_current_device())) return st;
+  if (validate_only) return PKV_OK;
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(shape->head_dim));
   AttnArgs a;
   a.q = q;
@@ -475,6 +477,12 @@ int paged_extend_attn_append(const void* q, const void* k_new, const void* v_new
           return set_error(PKV_ERR_INVALID_ARGUMENT, "%s: k_new / v_new overlap a pool", name);
   }
   if (shape->dtype != PKV_DTYPE_BF16 || plan->slot_blocks > kFuseMaxSlotBlocks) {
+    // the append kernel first, then the attention: every argument of both is
+    // checked before the append is launched
+    if ((st = extend_attn_call(name, q, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, nullptr,
+                               nullptr, nullptr, window, sm_scale, nullptr, 1, 1, 0, plan, shape, out, workspace,
+                               workspace_bytes, stream, nullptr, nullptr, true)))
+      return st;
     if ((st = pkv_append(k_new, v_new, k_pool, v_pool, page_table, page_table_stride, req_pool_indices, plan, shape,
                          stream)))
       return st;

@@ -561,3 +561,35 @@ def test_noalloc_refuses_plans_beyond_its_scratch():
     assert st == pkv.PKV_ERR_WORKSPACE and "static scratch" in lib.pkv_last_error().decode()
     assert lib.paged_extend_attn_noalloc(d, d, d, d, 2048, None, None, None, None, 0, 0.0, None, ctypes.byref(s), d,
                                          None) == pkv.PKV_ERR_INVALID_ARGUMENT
+
+
+def test_unfused_append_path_checks_attention_arguments_first():
+    """paged_extend_attn_append on a plan it does not fuse (slot_blocks > 128:
+    the append kernel runs first, then the attention) refuses a wrong window
+    or a short workspace before the append is launched: the status is the
+    argument error, not the device check the append would reach first (no GPU
+    here). Stand-in device pointers: nothing runs."""
+    lib = pkv.lib()
+    s = shape(64, 8, 128, 16, 5000)
+    p = pkv.build_extend_metadata([16384, 16384], [2048, 2048], s)
+    assert p.plan.slot_blocks > 128 and p.plan.workspace_bytes == 0
+    fake = p.plan
+    fake.qo_indptr, fake.kv_indptr, fake.prefix_lens, fake.items, fake.status = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    d = ctypes.c_void_p(0x1000)
+    kn, vn, kp, vp_ = (ctypes.c_void_p(a) for a in (0x100000, 0x8000000, 0x10000000, 0x80000000))
+
+    def call(window):
+        return lib.paged_extend_attn_append(d, kn, vn, kp, vp_, d, 2048, None, window, 0.0, ctypes.byref(fake),
+                                            ctypes.byref(s), d, None, 0, None)
+
+    assert call(7) == pkv.PKV_ERR_INVALID_ARGUMENT
+    assert "differs from the plan" in lib.pkv_last_error().decode()
+    assert call(0) == pkv.PKV_ERR_HIP   # every argument fine: stops at the device check
+    # a split plan on the unfused path with too little workspace
+    ps = pkv.build_extend_metadata([100000], [300], s)
+    assert ps.plan.slot_blocks > 128 and ps.plan.workspace_bytes > 0
+    fs = ps.plan
+    fs.qo_indptr, fs.kv_indptr, fs.prefix_lens, fs.items, fs.status = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    st = lib.paged_extend_attn_append(d, kn, vn, kp, vp_, d, 8192, None, 0, 0.0, ctypes.byref(fs), ctypes.byref(s),
+                                      d, d, 16, None)
+    assert st == pkv.PKV_ERR_WORKSPACE, lib.pkv_last_error().decode()
