@@ -150,10 +150,17 @@ __device__ inline bool key_visible(int j, int qpos, int kv_begin, int kv_end, in
 // zeros (a page id outside the pool).
 __device__ __attribute__((aligned(16))) const uint32_t g_zero_rows[64 * 4] = {};
 
-// Scores are kept relative to a per-row reference max m_ref (log2 units); it is
-// only raised when a row's true max exceeds it by more than this, so P = 2^(s-m_ref)
-// stays below 2^kRescaleSlack and the O rescale is rare.
-constexpr float kRescaleSlack = 8.f;
+// Scores are kept relative to a per-row reference m_ref (log2 units), set by
+// the row's first tile with a visible key to that tile's max. Later tiles are
+// weighted against the reference without taking their max (which costs 24
+// VALU instructions per wave and tile); only when some lane's sum of its 32
+// weights exceeds kLazyLimit does the tile get its scores again (recomputed:
+// the weights overwrote them) and its max, and every row of the wave whose
+// max beat its reference is raised to it (O and the running sum rescaled).
+// Every weight therefore stays at most 2^7, a reference trails its row's
+// running max by at most 7 (a larger gap makes a weight above 2^7: caught),
+// and it never exceeds that max, so no weight underflows because of it.
+constexpr float kLazyLimit = 128.f;
 
 // s_waitcnt immediate: vmcnt(N), lgkmcnt(0), expcnt unchanged (gfx9 encoding:
 // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -277,6 +284,7 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
   for (int db = 0; db < T::DBLK; ++db) o[db] = f32x16{};
   float m_ref = -INFINITY;  // reference max of this row, log2 units (scaled scores)
   float l_run = 0.f;        // running sum of 2^(s - m_ref) over the keys this lane holds
+  bool need_ref = true;     // (uniform) some row of the wave still has m_ref = -inf
 
   const int t0 = (it.kv_begin / T::BC) * T::BC;
   const int ntiles = it.kv_end > it.kv_begin ? (it.kv_end - t0 + T::BC - 1) / T::BC : 0;
@@ -599,7 +607,24 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
         s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(0, ks, kb2), qf[ks], s[kb2], 0, 0, 0);
     }
   };
-  auto seg_V = [&](int t) __attribute__((always_inline)) {
+  // scores of tile t once more, from K(t) in its LDS stage (intact until the
+  // gather of tile t+4, which comes after both groups' M(t)): the same
+  // fragments and MFMA order as the S(t) products, so the same bits
+  auto recompute_S = [&](int t) __attribute__((always_inline)) {
+    const uint32_t kst = uint32_t(t & (T::NSTAGE - 1)) * T::STAGE;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < T::KSTEPS; ++ks) {
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kst, ks, kb2), qf[ks], s[kb2], 0, 0, 0);
+        // (a rare path: one fragment read at a time, none hoisted into
+        // registers the rest of the loop needs)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  auto apply_mask = [&](int t) __attribute__((always_inline)) {
     const int kv0 = t0 + t * T::BC;
     // mask: element (kb2, j) is key kv0 + 32kb2 + 8(j/4) + 4half + j%4 of this lane's row
     const bool full = kv0 >= it.kv_begin && kv0 + T::BC <= it.kv_end && kv0 + T::BC - 1 <= qpos_first &&
@@ -626,14 +651,17 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
               (MASK && ((mw_cur[4 * kb2 + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0))
             s[kb2][j] = -INFINITY;
     }
+  };
+  // raise the reference of every row whose max over the tile beat it to that
+  // max (both halves of a row agree)
+  auto raise_ref = [&]() __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
     mx = other_half_max(mx) * c;   // this row's max over the tile, log2 units
-    // raise the reference only when the true max outruns it by more than the slack
-    const bool raise = mx > m_ref + kRescaleSlack;
+    const bool raise = mx > m_ref;
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float m_new = raise ? mx : m_ref;
       // lanes that keep their reference (possibly still -inf) must not compute -inf - -inf
@@ -643,18 +671,47 @@ __global__ __launch_bounds__(64 * kWavesBf16, 2) void extend_attn_bf16(const Par
       for (int db = 0; db < T::DBLK; ++db) o[db] *= alpha;
       m_ref = m_new;
     }
-    const float m_off = m_ref == -INFINITY ? 0.f : m_ref;
-    // P = exp2(S*c - m_ref) in bf16, laid out as the B operand of O^T += V^T P^T
-    float lsum = 0.f;
+  };
+  // P = exp2(S*c - m_off), in place over the scores (fp32); returns the sum of
+  // this lane's 32 weights
+  auto exp_in_place = [&](float m_off) __attribute__((always_inline)) {
+    float sum = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float pj = fast_exp2(fmaf(s[kb2][j], c, -m_off));
-        lsum += pj;
-        pb[kb2][j >> 3][j & 7] = (__bf16)pj;
+        s[kb2][j] = fast_exp2(fmaf(s[kb2][j], c, -m_off));
+        sum += s[kb2][j];
       }
+    return sum;
+  };
+  // Softmax segment: a tile is weighted against the current references; a
+  // caught tile (kLazyLimit) gets its scores again and raises them, as do the
+  // tiles of a wave with a row still lacking a reference (one site for the O
+  // rescale).
+  auto seg_V = [&](int t) __attribute__((always_inline)) {
+    apply_mask(t);
+    float lsum = 0.f;
+    bool with_max = need_ref;   // (uniform)
+    if (!with_max) {
+      lsum = exp_in_place(m_ref);
+      if (__builtin_amdgcn_ballot_w64(lsum > kLazyLimit)) {
+        recompute_S(t);
+        apply_mask(t);
+        with_max = true;
+      }
+    }
+    if (with_max) {
+      raise_ref();
+      need_ref = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+      lsum = exp_in_place(m_ref == -INFINITY ? 0.f : m_ref);
+    }
     l_run += lsum;
+    // P in bf16, laid out as the B operand of O^T += V^T P^T
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pb[kb2][j >> 3][j & 7] = (__bf16)s[kb2][j];
   };
   // segment M: O += V(t)^T P(t) and S(t+1) = K(t+1) Q^T, as one straight run of
   // MFMAs. Even step 2i is PV product i (d-block i % DBLK, key quarter i / DBLK),

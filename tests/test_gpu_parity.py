@@ -204,6 +204,59 @@ def test_split_partials_precision(q_scale):
           f"(mean {float(d.mean()):.3e})", flush=True)
 
 
+@pytest.mark.parametrize("case,window,spike,q_scale", [
+    ("keys x40 at 1000..1015", 0, (1000, 1016, 40.0), 1.0),
+    ("keys x40 inside a window", 600, (1900, 1916, 40.0), 1.0),
+    ("q x8, window", 300, None, 8.0),
+])
+def test_reference_raised_on_large_scores(case, window, spike, q_scale):
+    """Scores that jump far past a row's reference after its first tiles: a
+    block of 16 keys scaled by 40 (their weights against the old reference
+    overflow to inf before the tile is caught), or q scaled by 8 under a
+    sliding window (a row's first tile holds few of its keys, so its reference
+    starts low and later tiles' weights sum past the catch limit). A 2048 + 512
+    request, split over the GPU; the plain launch (append kernel first) and the
+    fused one against the oracle, and bitwise equal to each other."""
+    P, L = np.array([2048], np.int32), np.array([512], np.int32)
+    pages = 200
+    w = wl.Workload("large scores", 47, "bf16", 16, 4, 128, 64, pages, window, P, L,
+                    wl.shuffled_page_table(47, pages, P + L, 64))
+    kp, vp = oracle_pools(w)
+    slots = []
+    if spike is not None:
+        lo, hi, factor = spike
+        for pos in range(lo, hi):   # prefix positions: written by fill_prefix
+            page, slot = int(w.page_table[0][pos // 64]), pos % 64
+            kp[page, slot] = wl.to_storage(wl.values(kp[page, slot], "bf16") * np.float32(factor), "bf16")
+            slots.append((page, slot))
+    qv = wl.values(w.q_all(), "bf16") * np.float32(q_scale)
+    q_bits = wl.to_storage(qv, "bf16")
+    ref = oracle.extend_attention(wl.values(q_bits, "bf16"), wl.values(kp, "bf16"), wl.values(vp, "bf16"),
+                                  w.page_table, w.prefix_lens, w.chunk_lens, window=window)
+
+    def cache_with_spike():
+        c = DeviceCache(w)
+        c.fill_prefix(w)
+        for page, slot in slots:
+            c.k_pool[page, slot] = torch.from_numpy(kp[page, slot].view(np.int16).copy()).cuda().view(torch.bfloat16)
+        return c
+
+    q = torch.from_numpy(q_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    c1 = cache_with_spike()
+    plan = c1.append_step(w)
+    assert plan.plan.n_split_rows > 0, "expected split items"
+    plain = pkv.paged_extend_attn(q, c1.k_pool, c1.v_pool, c1.page_table, plan)
+    c2 = cache_with_spike()
+    fplan = pkv.build_extend_metadata(P, L, shape_of(w), window, 0, device="cuda")
+    kn, vn = c2._gather_new_kv(w)
+    fused = pkv.paged_extend_attn_append(q, kn, vn, c2.k_pool, c2.v_pool, c2.page_table, fplan)
+    torch.cuda.synchronize()
+    assert fplan.plan.slot_blocks <= 128, "expected the fused launch"
+    check(f"large scores, {case}: plain", plain, ref, "bf16")
+    check(f"large scores, {case}: fused", fused, ref, "bf16")
+    assert torch.equal(plain.view(torch.int16), fused.view(torch.int16)), "plain and fused launches differ"
+
+
 # configs 4 and 5 at full size: every row, in test_gpu_full_size.py
 
 
